@@ -1,0 +1,59 @@
+"""The seeded input generators: determinism, per-head independence, BF16
+rounding, and the shape/structure of each workload (CPU only)."""
+
+import numpy as np
+
+from long_sequence_dense_amd import inputs
+
+
+def test_bf16_round_to_nearest_even():
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9, -2.5, 0.0, -0.0],
+                 dtype=np.float32)
+    b = inputs.f32_to_bf16_bits(x)
+    back = inputs.bf16_bits_to_f32(b)
+    # 1+2^-8 is a tie between 1 and 1+2^-7 -> even (1); 1+3*2^-8 -> 1+2^-6
+    assert list(back) == [1.0, 1.0, 1.0 + 2.0 ** -6, 1.0, -2.5, 0.0, -0.0]
+    assert b[6] == 0x8000
+    rng = np.random.default_rng(0)
+    y = rng.standard_normal(10000).astype(np.float32)
+    err = np.abs(inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(y)) - y)
+    assert np.all(err <= np.abs(y) * 2.0 ** -8)
+
+
+def test_deterministic_and_head_independent():
+    cfg = inputs.CONFIGS["tiny"]
+    a = inputs.make_tensor(cfg, "k")
+    b = inputs.make_tensor(cfg, "k", heads=[1])
+    assert np.array_equal(a[1], b[0])
+    assert np.array_equal(a, inputs.make_tensor(cfg, "k"))
+    assert not np.array_equal(a[0], a[1])
+
+
+def test_tiny_key_offset():
+    d = inputs.make_inputs("tiny")
+    k = inputs.bf16_bits_to_f32(d["k"]).astype(np.float64)
+    q = inputs.bf16_bits_to_f32(d["q"]).astype(np.float64)
+    assert d["k"].shape == (2, 1024, 128)
+    # per-channel means of K carry the N(0, 2) offset, Q's do not
+    assert np.std(k.mean(axis=1)) > 0.8
+    assert np.std(q.mean(axis=1)) < 0.1
+
+
+def test_outlier_structure_small():
+    cfg = inputs.CONFIGS["fp4"].with_shape(H=3, L=2048)
+    q = inputs.bf16_bits_to_f32(inputs.make_tensor(cfg, "q")).astype(np.float64)
+    v = inputs.bf16_bits_to_f32(inputs.make_tensor(cfg, "v")).astype(np.float64)
+    for h in range(3):
+        ch = inputs.outlier_channels(cfg, h)
+        assert len(ch) == 3
+        med = np.median(np.abs(q[h]), axis=0)
+        others = np.setdiff1d(np.arange(128), ch)
+        assert np.all(med[ch] > 10 * np.max(med[others]))
+    assert abs(np.std(v) - 1.0) < 0.05
+
+
+def test_sample_rows():
+    r = inputs.sample_rows(109000, 64)
+    assert r.min() >= 0 and r.max() == 108999 and len(set(r)) == len(r)
+    for t in (64, 128, 256):
+        assert (108999 // t) * t in r
