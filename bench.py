@@ -1,0 +1,232 @@
+"""Benchmark of the dense long-sequence attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input at the 15-second
+clip scale (H = 40 heads, L = 109,000 tokens, d = 128):
+  attn_fwd_bf16 on the BF16 workload (N(0,1), 3 of 128 channels x20 on Q, K),
+  qk_prep_fp4 + attn_fwd_fp4qk on the FP4 workload (Student-t(3) Q, K with the
+  same outliers, N(0,1) V).
+value = attention FLOP of the step (2 x 4 H L^2 d) / step time, TFLOP/s.
+Prints ONE JSON line (rank 0).  Inputs are resident in HBM before timing.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense BF16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "attention TFLOP/s and % of MFMA peak at 109k tokens, BF16 and FP4-QK paths"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_flop(H, L, d=128):
+    return 4.0 * H * float(L) * float(L) * d
+
+
+def prep_bytes(H, L, d=128):
+    # read Q and K once (2 B each) + write codes (d/2 B) and scales (d/16 B) for both
+    return H * L * (2 * 2 * d + 2 * (d // 2 + d // 16))
+
+
+def gen_inputs(torch, name):
+    from long_sequence_dense_amd import inputs
+    cfg = inputs.CONFIGS[name]
+    out = {}
+    for which in ("q", "k", "v"):
+        t0 = time.time()
+        bits = inputs.make_tensor(cfg, which)
+        out[which] = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        del bits
+        log("  %s.%s generated and uploaded in %.1f s" % (name, which, time.time() - t0))
+    return cfg, out
+
+
+def cpu_baseline(H, L, d, seconds_budget=20.0):
+    """Time the CPU oracle (as it stands) on a bounded sample of the workload and
+    extrapolate a full step; returns the cpu_baseline object."""
+    from long_sequence_dense_amd import inputs
+    from oracle.attention import attention_fp64
+    from oracle.nvfp4 import qk_prep_fp4
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    cfg = inputs.CONFIGS["clip15s"]
+    heads = [0, 1]
+    rows = inputs.sample_rows(L, 384)
+    q = inputs.make_tensor(cfg, "q", heads)
+    k = inputs.make_tensor(cfg, "k", heads)
+    v = inputs.make_tensor(cfg, "v", heads)
+    f = lambda b: inputs.bf16_bits_to_f32(b).astype(np.float64)
+    t0 = time.time()
+    attention_fp64(f(q), f(k), f(v), cfg.scale, rows=rows)
+    t_attn = time.time() - t0
+    attn_rate = len(heads) * len(rows) * 4.0 * L * d / t_attn          # FLOP/s
+    fcfg = inputs.CONFIGS["fp4"]
+    qf = inputs.make_tensor(fcfg, "q", [0])
+    kf = inputs.make_tensor(fcfg, "k", [0])
+    t0 = time.time()
+    qk_prep_fp4(qf, kf)
+    t_prep_head = time.time() - t0
+    full_attn_s = attn_flop(H, L, d) / attn_rate
+    step_s = 2 * full_attn_s + H * t_prep_head
+    return {
+        "value": round(2 * attn_flop(H, L, d) / step_s / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": ("fp64 numpy oracle: BF16 attention for %d query rows x %d heads at L=%d "
+                   "(%.1f s, %.2f GFLOP/s), NVFP4 prep of 1 full head of Q and K (%.1f s); "
+                   "full step extrapolated to %.0f s (2 attention calls + %d heads of prep)"
+                   % (len(rows), len(heads), L, t_attn, attn_rate / 1e9, t_prep_head, step_s, H)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "bf16"], default="all",
+                    help="bf16: time only attn_fwd_bf16 (for profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(attention would shard by head with no exchange); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_sequence_dense_amd import binding
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    binding.load_library()
+    H, L, d = 40, 109000, 128
+
+    log("generating inputs (seeded, synthetic) ...")
+    cfg4, x4 = gen_inputs(torch, "clip15s")
+    cfg5, x5 = gen_inputs(torch, "fp4")
+    dev = x4["q"].device
+    o4 = torch.empty((H, L, d), dtype=torch.bfloat16, device=dev)
+    o5 = torch.empty((H, L, d), dtype=torch.bfloat16, device=dev)
+    prep = {
+        "q_codes": torch.empty((H, L, d // 2), dtype=torch.uint8, device=dev),
+        "q_scales": torch.empty((H, L, d // 16), dtype=torch.uint8, device=dev),
+        "k_codes": torch.empty((H, L, d // 2), dtype=torch.uint8, device=dev),
+        "k_scales": torch.empty((H, L, d // 16), dtype=torch.uint8, device=dev),
+        "k_mean": torch.empty((H, d), dtype=torch.float32, device=dev),
+    }
+    ws = torch.empty(binding.qk_prep_fp4_workspace_bytes(H, L, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = {n: [] for n in ("bf16", "prep", "fp4")}
+
+    def step(record):
+        def mark():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            return e
+        a = mark() if record else None
+        binding.attn_fwd_bf16(x4["q"], x4["k"], x4["v"], o4, None, cfg4.scale, stream)
+        if args.only == "bf16":
+            if record:
+                ev["bf16"].append((a, mark()))
+            return
+        b = mark() if record else None
+        binding.qk_prep_fp4(x5["q"], x5["k"], prep, ws, stream)
+        c = mark() if record else None
+        binding.attn_fwd_fp4qk(prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"],
+                               x5["v"], o5, None, cfg5.scale, stream)
+        if record:
+            e = mark()
+            ev["bf16"].append((a, b))
+            ev["prep"].append((b, c))
+            ev["fp4"].append((c, e))
+
+    log("warmup %d steps ..." % args.warmup)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log("timing %d steps ..." % args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log("timed region %.2f s" % wall)
+    assert not torch.isnan(o4).any().item() and not torch.isnan(o5).any().item()
+
+    def avg_ms(name):
+        xs = [a.elapsed_time(b) for a, b in ev[name]]
+        return sum(xs) / len(xs) if xs else None
+
+    ms_step = wall * 1e3 / args.steps
+    fl = attn_flop(H, L, d)
+    step_flop = fl if args.only == "bf16" else 2 * fl
+    value = step_flop / (ms_step * 1e-3) / 1e12
+    t_bf16 = avg_ms("bf16")
+    achieved = fl / (t_bf16 * 1e-3) / 1e12
+    paths = {"attn_fwd_bf16": {"ms": round(t_bf16, 3), "TFLOP/s": round(achieved, 1),
+                               "frac_of_peak": round(achieved / PEAK_BF16_TFLOPS, 4)}}
+    if args.only != "bf16":
+        t_prep, t_fp4 = avg_ms("prep"), avg_ms("fp4")
+        gbs = prep_bytes(H, L, d) / (t_prep * 1e-3) / 1e9
+        a4 = fl / (t_fp4 * 1e-3) / 1e12
+        paths["qk_prep_fp4"] = {"ms": round(t_prep, 4), "GB/s": round(gbs, 1),
+                                "algorithmic_bytes": prep_bytes(H, L, d),
+                                "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        paths["attn_fwd_fp4qk"] = {"ms": round(t_fp4, 3), "TFLOP/s": round(a4, 1),
+                                   "frac_of_peak": round(a4 / PEAK_BF16_TFLOPS, 4),
+                                   "mfma_precision": "bf16 (exact dequantization of NVFP4 Q/K)"}
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json")
+    if os.path.exists(tpath):
+        try:
+            traffic = json.load(open(tpath)).get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws, BF16)",
+        "config": {"workload": "dense non-causal attention, 15-second clip scale: BF16 path + "
+                               "NVFP4 prep + FP4-QK path" if args.only != "bf16" else "BF16 path only",
+                   "H": H, "L": L, "d": d, "softmax_scale": "1/sqrt(128)",
+                   "bf16_inputs": cfg4.desc, "fp4_inputs": cfg5.desc},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_flop_per_launch": fl},
+        "paths": paths,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(H, L, d)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

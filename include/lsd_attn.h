@@ -1,0 +1,138 @@
+/*
+ * lsd_attn.h - dense long-sequence attention on AMD MI355X (gfx950).
+ *
+ * C ABI of liblsd_attn.so.  Three operations over per-head token tensors
+ * laid out [H, L, d] (row-major: head, token, channel), d = 128:
+ *
+ *   attn_fwd_bf16   dense non-causal softmax attention, BF16 in and out.
+ *   qk_prep_fp4     mean-key subtraction, shared 128-point Hadamard rotation
+ *                   and NVFP4 block quantization of Q and K.
+ *   attn_fwd_fp4qk  attention whose scores come from the NVFP4 Q and K;
+ *                   probabilities and V stay BF16.
+ *
+ * The method is the one of "Pika H3 Flex in FastVideo: 7x Faster, and Near
+ * Real Time in 4-bit" (haoailab blog): section "Faster at BF16" (dense
+ * attention over the ~109k-token joint sequence of a 15-second clip) and
+ * section "FP4 attention" (smooth K, rotate Q and K with one orthonormal
+ * Hadamard matrix, E2M1 values with one E4M3 scale per 16 channels and unit
+ * global scale, a fused kernel that applies the transforms while quantizing).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer to contiguous memory owned by
+ *     the caller.  BF16 values are passed as their uint16 bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued asynchronously on it; nothing synchronizes.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     returned as an lsd_status; a launch failure returns LSD_ERR_LAUNCH.  A
+ *     device fault surfaces at the caller's next synchronization.  Nothing is
+ *     printed and no exception crosses the ABI.
+ *   - The library allocates no memory and keeps no state between calls;
+ *     concurrent calls on different streams are safe as long as their output
+ *     (and workspace) buffers do not overlap.
+ *   - Limits: d must be 128; H >= 1; L >= 1; H * L <= 2^31 - 1.  Tensor
+ *     pointers must be 16-byte aligned.
+ *   - Inputs must be finite.  NaN or Inf in any input, or inputs so large that
+ *     the rotation overflows float32 (|x| around 2^120), give unspecified
+ *     output (no fault).
+ */
+#ifndef LSD_ATTN_H
+#define LSD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum lsd_status {
+  LSD_OK = 0,
+  LSD_ERR_NULL = 1,           /* a required pointer is NULL                   */
+  LSD_ERR_SHAPE = 2,          /* H < 1, L < 1 or H * L too large              */
+  LSD_ERR_UNSUPPORTED_D = 3,  /* d != 128                                     */
+  LSD_ERR_ALIGN = 4,          /* a tensor pointer is not 16-byte aligned      */
+  LSD_ERR_WORKSPACE = 5,      /* workspace missing, misaligned or too small   */
+  LSD_ERR_LAUNCH = 6,         /* the HIP runtime rejected a kernel launch     */
+  LSD_ERR_SCALE = 7           /* softmax_scale is not finite and positive     */
+};
+
+/* Version of this ABI (the value of LSD_ABI_VERSION the library was built with). */
+#define LSD_ABI_VERSION 1
+int lsd_abi_version(void);
+
+/* Static description of a status code ("ok", "null pointer", ...). */
+const char* lsd_status_str(int status);
+
+/*
+ * attn_fwd_bf16 - O = softmax(softmax_scale * Q K^T) V for every head, no mask.
+ *   q, k, v : [H, L, d] BF16 bits, read only.
+ *   o       : [H, L, d] BF16 bits, written (round to nearest even of the fp32
+ *             result).  Must not alias q, k or v.
+ *   lse     : optional [H, L] float32 natural-log log-sum-exp of the scaled
+ *             scores of each query row (NULL to skip).
+ *   softmax_scale : sigma > 0 applied to the fp32 scores.
+ * Scores and the P.V products accumulate in fp32 on the matrix cores; P is
+ * rounded to BF16 before P.V.  Results are deterministic (no atomics).
+ * Source: "Faster at BF16" (dense attention over all tokens of a clip).
+ */
+int attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  uint16_t* o, float* lse, int H, int L, int d,
+                  float softmax_scale, void* stream);
+
+/*
+ * Bytes of device workspace qk_prep_fp4 needs for this shape (0 on a bad
+ * shape).  It holds exact per-(head, channel, exponent) integer partial sums
+ * of K.
+ */
+size_t qk_prep_fp4_workspace_bytes(int H, int L, int d);
+
+/*
+ * qk_prep_fp4 - quantize Q and K for attn_fwd_fp4qk.
+ *   q, k      : [H, L, d] BF16 bits, read only.
+ *   q_codes, k_codes   : [H, L, d/2] uint8, written; byte j of a row holds the
+ *                        E2M1 code of channel 2j in its low nibble and of
+ *                        channel 2j+1 in its high nibble (bit 3 = sign).
+ *   q_scales, k_scales : [H, L, d/16] uint8, written; OCP E4M3 bits of the
+ *                        scale of channels 16b..16b+15 (never NaN, <= 448).
+ *   k_mean    : [H, d] float32, written: per head and channel the mean of K
+ *               over the L tokens, RN32(RN64(exact sum) / L).
+ *   workspace : device buffer of at least qk_prep_fp4_workspace_bytes(H,L,d)
+ *               bytes, 256-byte aligned; contents on entry are ignored and on
+ *               return are unspecified.
+ * Per row: K only: x = RN32(k - k_mean); then the in-order Sylvester butterfly
+ * in fp32 (7 stages, stage s pairs channels i and i + 2^s), times
+ * RN32(1/sqrt(128)); per 16-channel block the scale is the E4M3 value nearest
+ * to max|y|/6 (ties to even, saturating at 448) and each code is the E2M1
+ * value nearest to y/scale (ties to even, saturating at 6, sign kept, all
+ * codes signed zero when the scale is 0).  Codes and scales are exact
+ * functions of the inputs: bit-identical from run to run.
+ * Source: "FP4 attention" (smooth K, rotate Q and K, E2M1 + E4M3 per 16).
+ */
+int qk_prep_fp4(const uint16_t* q, const uint16_t* k,
+                uint8_t* q_codes, uint8_t* q_scales,
+                uint8_t* k_codes, uint8_t* k_scales,
+                float* k_mean, void* workspace, size_t workspace_bytes,
+                int H, int L, int d, void* stream);
+
+/*
+ * attn_fwd_fp4qk - attention on quantized Q and K.
+ *   q_codes, q_scales, k_codes, k_scales : as written by qk_prep_fp4.
+ *   v   : [H, L, d] BF16 bits.   o : [H, L, d] BF16 bits, written.
+ *   lse : optional [H, L] float32 (NULL to skip).
+ * Scores are softmax_scale * (Qhat . Khat) where Qhat, Khat are the exact
+ * dequantized values (E2M1 times E4M3: at most 6 significant bits, so exact in
+ * BF16); the rest is as in attn_fwd_bf16.  Because the smoothing and the
+ * orthonormal rotation change no score before quantization, O approximates
+ * attn_fwd_bf16 on the original Q, K.
+ * Source: "FP4 attention" (queries and keys quantized, P and V in BF16).
+ */
+int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales,
+                   const uint8_t* k_codes, const uint8_t* k_scales,
+                   const uint16_t* v, uint16_t* o, float* lse,
+                   int H, int L, int d, float softmax_scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSD_ATTN_H */

@@ -1,0 +1,177 @@
+"""ctypes binding of liblsd_attn.so: same names as the C ABI, argument
+marshalling only.  Every computation runs in the library's HIP kernels; there
+is no fallback of any kind: if the library is missing or fails to load, every
+call raises.
+
+Tensors are torch tensors on a ROCm device (torch provides device memory and
+the current stream, nothing else).  BF16 tensors may be torch.bfloat16 or
+torch.uint16/int16 holding BF16 bit patterns.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblsd_attn.so")
+HEAD_DIM = 128
+
+STATUS = {
+    0: "LSD_OK", 1: "LSD_ERR_NULL", 2: "LSD_ERR_SHAPE", 3: "LSD_ERR_UNSUPPORTED_D",
+    4: "LSD_ERR_ALIGN", 5: "LSD_ERR_WORKSPACE", 6: "LSD_ERR_LAUNCH", 7: "LSD_ERR_SCALE",
+}
+
+# name -> (restype, argtypes); mirrors include/lsd_attn.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+SIGNATURES = {
+    "lsd_abi_version": (_I, []),
+    "lsd_status_str": (ctypes.c_char_p, [_I]),
+    "attn_fwd_bf16": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
+    "qk_prep_fp4_workspace_bytes": (_S, [_I, _I, _I]),
+    "qk_prep_fp4": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _P]),
+    "attn_fwd_fp4qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
+}
+
+_lib = None
+
+
+class LsdError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS.get(status, status), msg))
+        self.status = status
+
+
+def load_library(path=None):
+    """Load (once) and return the ctypes handle; raises if it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("liblsd_attn.so is not built (%s); run "
+                           "`python -m long_sequence_dense_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status):
+    return load_library().lsd_status_str(int(status)).decode()
+
+
+def _check(fn, st):
+    if st != 0:
+        raise LsdError(fn, st, status_str(st))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtypes, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU, got %s" % (name, t.device))
+    if t.dtype not in dtypes:
+        raise TypeError("%s: dtype %s not in %s" % (name, t.dtype, dtypes))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _bf16_types():
+    import torch
+    return (torch.bfloat16, torch.uint16, torch.int16)
+
+
+def attn_fwd_bf16(q, k, v, o=None, lse=None, softmax_scale=None, stream=None):
+    """O = softmax(scale * Q K^T) V per head; q, k, v [H, L, 128] BF16."""
+    import torch
+    H, L, d = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, n, _bf16_types(), (H, L, d))
+    if o is None:
+        o = torch.empty((H, L, d), dtype=torch.bfloat16, device=q.device)
+    _need(o, "o", _bf16_types(), (H, L, d))
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), (H, L))
+    scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    st = load_library().attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                      H, L, d, scale, _stream(stream))
+    _check("attn_fwd_bf16", st)
+    return o
+
+
+def qk_prep_fp4_workspace_bytes(H, L, d=HEAD_DIM):
+    return int(load_library().qk_prep_fp4_workspace_bytes(H, L, d))
+
+
+def qk_prep_fp4(q, k, out=None, workspace=None, stream=None):
+    """Mean-K, Hadamard and NVFP4 quantization of Q and K ([H, L, 128] BF16).
+    Returns dict(q_codes, q_scales, k_codes, k_scales, k_mean)."""
+    import torch
+    H, L, d = q.shape
+    _need(q, "q", _bf16_types(), (H, L, d))
+    _need(k, "k", _bf16_types(), (H, L, d))
+    dev = q.device
+    if out is None:
+        out = {
+            "q_codes": torch.empty((H, L, d // 2), dtype=torch.uint8, device=dev),
+            "q_scales": torch.empty((H, L, d // 16), dtype=torch.uint8, device=dev),
+            "k_codes": torch.empty((H, L, d // 2), dtype=torch.uint8, device=dev),
+            "k_scales": torch.empty((H, L, d // 16), dtype=torch.uint8, device=dev),
+            "k_mean": torch.empty((H, d), dtype=torch.float32, device=dev),
+        }
+    for n in ("q_codes", "k_codes"):
+        _need(out[n], n, (torch.uint8,), (H, L, d // 2))
+    for n in ("q_scales", "k_scales"):
+        _need(out[n], n, (torch.uint8,), (H, L, d // 16))
+    _need(out["k_mean"], "k_mean", (torch.float32,), (H, d))
+    need = qk_prep_fp4_workspace_bytes(H, L, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load_library().qk_prep_fp4(
+        _ptr(q), _ptr(k), _ptr(out["q_codes"]), _ptr(out["q_scales"]), _ptr(out["k_codes"]),
+        _ptr(out["k_scales"]), _ptr(out["k_mean"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), H, L, d, _stream(stream))
+    _check("qk_prep_fp4", st)
+    return out
+
+
+def attn_fwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o=None, lse=None,
+                   softmax_scale=None, stream=None):
+    """Attention with scores from NVFP4 Q/K (as written by qk_prep_fp4)."""
+    import torch
+    H, L, d = v.shape
+    _need(v, "v", _bf16_types(), (H, L, d))
+    for n, t in (("q_codes", q_codes), ("k_codes", k_codes)):
+        _need(t, n, (torch.uint8,), (H, L, d // 2))
+    for n, t in (("q_scales", q_scales), ("k_scales", k_scales)):
+        _need(t, n, (torch.uint8,), (H, L, d // 16))
+    if o is None:
+        o = torch.empty((H, L, d), dtype=torch.bfloat16, device=v.device)
+    _need(o, "o", _bf16_types(), (H, L, d))
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), (H, L))
+    scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    st = load_library().attn_fwd_fp4qk(_ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales),
+                                       _ptr(v), _ptr(o), _ptr(lse), H, L, d, scale, _stream(stream))
+    _check("attn_fwd_fp4qk", st)
+    return o

@@ -1,0 +1,97 @@
+// C ABI of liblsd_attn.so: host-side argument checks, then the launches.
+// The declarations, argument meanings, layouts and error behaviour are in
+// include/lsd_attn.h.
+#include <cmath>
+#include <climits>
+
+#include "../../include/lsd_attn.h"
+#include "lsd_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int H, int L, int d) {
+  if (d != lsd::kHeadDim) return LSD_ERR_UNSUPPORTED_D;
+  if (H < 1 || L < 1) return LSD_ERR_SHAPE;
+  if ((long long)H * (long long)L > (long long)INT_MAX) return LSD_ERR_SHAPE;
+  return LSD_OK;
+}
+
+int check_scale(float s) { return (std::isfinite(s) && s > 0.0f) ? LSD_OK : LSD_ERR_SCALE; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? LSD_OK : LSD_ERR_LAUNCH; }
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+}  // namespace
+
+extern "C" {
+
+int lsd_abi_version(void) { return LSD_ABI_VERSION; }
+
+const char* lsd_status_str(int status) {
+  switch (status) {
+    case LSD_OK: return "ok";
+    case LSD_ERR_NULL: return "null pointer argument";
+    case LSD_ERR_SHAPE: return "bad shape (need H >= 1, L >= 1, H*L <= 2^31-1)";
+    case LSD_ERR_UNSUPPORTED_D: return "unsupported head dimension (only d = 128)";
+    case LSD_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case LSD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case LSD_ERR_LAUNCH: return "kernel launch failed";
+    case LSD_ERR_SCALE: return "softmax_scale must be finite and > 0";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                  int H, int L, int d, float softmax_scale, void* stream) {
+  int st = check_shape(H, L, d);
+  if (st != LSD_OK) return st;
+  if (!q || !k || !v || !o) return LSD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LSD_ERR_ALIGN;
+  if (lse && ((uintptr_t)lse & 3u)) return LSD_ERR_ALIGN;
+  if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_attn_bf16(q, k, v, o, lse, H, L, softmax_scale * kLog2e,
+                                             (hipStream_t)stream));
+}
+
+size_t qk_prep_fp4_workspace_bytes(int H, int L, int d) {
+  if (check_shape(H, L, d) != LSD_OK) return 0;
+  return lsd::prep_workspace_bytes(H);
+}
+
+int qk_prep_fp4(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8_t* q_scales,
+                uint8_t* k_codes, uint8_t* k_scales, float* k_mean, void* workspace,
+                size_t workspace_bytes, int H, int L, int d, void* stream) {
+  int st = check_shape(H, L, d);
+  if (st != LSD_OK) return st;
+  if (!q || !k || !q_codes || !q_scales || !k_codes || !k_scales || !k_mean) return LSD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_codes) || !aligned16(q_scales) ||
+      !aligned16(k_codes) || !aligned16(k_scales) || !aligned16(k_mean))
+    return LSD_ERR_ALIGN;
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lsd::prep_workspace_bytes(H))
+    return LSD_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_qk_prep(q, k, q_codes, q_scales, k_codes, k_scales, k_mean, workspace,
+                                           H, L, (hipStream_t)stream));
+}
+
+int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                   const uint8_t* k_scales, const uint16_t* v, uint16_t* o, float* lse, int H, int L,
+                   int d, float softmax_scale, void* stream) {
+  int st = check_shape(H, L, d);
+  if (st != LSD_OK) return st;
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v || !o) return LSD_ERR_NULL;
+  if (!aligned16(q_codes) || !aligned16(q_scales) || !aligned16(k_codes) || !aligned16(k_scales) ||
+      !aligned16(v) || !aligned16(o))
+    return LSD_ERR_ALIGN;
+  if (lse && ((uintptr_t)lse & 3u)) return LSD_ERR_ALIGN;
+  if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_attn_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, H, L,
+                                              softmax_scale * kLog2e, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+symbol include/lsd_attn.h declares, and rejects bad arguments with the
+documented status before anything is enqueued (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_sequence_dense_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsd_attn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("library not built")
+    return binding.load_library()
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(binding.SIGNATURES)
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.lsd_abi_version() == 1
+    for st in range(8):
+        assert lib.lsd_status_str(st).decode()
+    assert lib.lsd_status_str(99).decode() == "unknown status"
+
+
+def test_workspace_query(lib):
+    assert lib.qk_prep_fp4_workspace_bytes(40, 109000, 128) == 40 * 128 * 256 * 8
+    assert lib.qk_prep_fp4_workspace_bytes(0, 10, 128) == 0
+    assert lib.qk_prep_fp4_workspace_bytes(1, 10, 64) == 0
+
+
+A = ctypes.c_void_p(0x100000)       # fake, 16-byte aligned, never dereferenced
+B = ctypes.c_void_p(0x100008)       # 8-byte aligned only
+N = ctypes.c_void_p(0)
+
+
+def test_attn_bf16_argument_errors(lib):
+    f = lib.attn_fwd_bf16
+    assert f(A, A, A, A, N, 2, 16, 64, 0.1, N) == 3            # d
+    assert f(A, A, A, A, N, 0, 16, 128, 0.1, N) == 2           # H
+    assert f(A, A, A, A, N, 2, 0, 128, 0.1, N) == 2            # L
+    assert f(A, A, A, A, N, 70000, 70000, 128, 0.1, N) == 2    # H*L overflow
+    assert f(N, A, A, A, N, 2, 16, 128, 0.1, N) == 1           # null q
+    assert f(A, A, A, N, N, 2, 16, 128, 0.1, N) == 1           # null o
+    assert f(A, B, A, A, N, 2, 16, 128, 0.1, N) == 4           # misaligned k
+    assert f(A, A, A, A, A, 2, 16, 128, 0.0, N) == 7           # scale 0
+    assert f(A, A, A, A, A, 2, 16, 128, float("nan"), N) == 7
+    assert f(A, A, A, A, A, 2, 16, 128, float("inf"), N) == 7
+
+
+def test_prep_argument_errors(lib):
+    f = lib.qk_prep_fp4
+    ws = ctypes.c_void_p(0x200000)
+    need = lib.qk_prep_fp4_workspace_bytes(2, 16, 128)
+    assert f(A, A, A, A, A, A, A, ws, need, 2, 16, 64, N) == 3
+    assert f(A, A, A, A, A, A, N, ws, need, 2, 16, 128, N) == 1          # null k_mean
+    assert f(A, A, A, B, A, A, A, ws, need, 2, 16, 128, N) == 4          # misaligned scales
+    assert f(A, A, A, A, A, A, A, N, need, 2, 16, 128, N) == 5           # null workspace
+    assert f(A, A, A, A, A, A, A, ws, need - 1, 2, 16, 128, N) == 5      # too small
+    assert f(A, A, A, A, A, A, A, ctypes.c_void_p(0x200010), need, 2, 16, 128, N) == 5  # not 256-aligned
+
+
+def test_fp4qk_argument_errors(lib):
+    f = lib.attn_fwd_fp4qk
+    assert f(A, A, A, A, A, A, N, 2, 16, 128, -1.0, N) == 7
+    assert f(A, A, N, A, A, A, N, 2, 16, 128, 0.1, N) == 1
+    assert f(A, A, A, A, A, B, N, 2, 16, 128, 0.1, N) == 4
+    assert f(A, A, A, A, A, A, N, 2, 16, 256, 0.1, N) == 3
+
+
+def test_missing_library_raises(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load_library(str(tmp_path / "nope.so"))
