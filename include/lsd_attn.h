@@ -29,8 +29,9 @@
  *   - The library allocates no memory and keeps no state between calls;
  *     concurrent calls on different streams are safe as long as their output
  *     (and workspace) buffers do not overlap.
- *   - Limits: d must be 128; H >= 1; L >= 1; H * L <= 2^31 - 1.  Tensor
- *     pointers must be 16-byte aligned.
+ *   - Limits: d must be 128; H >= 1; L >= 1; H * L <= 2^31 - 1; for the two
+ *     attention calls also L < 2^23 (one head's rows are addressed with
+ *     32-bit byte offsets).  Tensor pointers must be 16-byte aligned.
  *   - Inputs must be finite.  NaN or Inf in any input, or inputs so large that
  *     the rotation overflows float32 (|x| around 2^120), give unspecified
  *     output (no fault).
@@ -48,7 +49,7 @@ extern "C" {
 enum lsd_status {
   LSD_OK = 0,
   LSD_ERR_NULL = 1,           /* a required pointer is NULL                   */
-  LSD_ERR_SHAPE = 2,          /* H < 1, L < 1 or H * L too large              */
+  LSD_ERR_SHAPE = 2,          /* H < 1, L < 1, H * L or (attention) L too large */
   LSD_ERR_UNSUPPORTED_D = 3,  /* d != 128                                     */
   LSD_ERR_ALIGN = 4,          /* a tensor pointer is not 16-byte aligned      */
   LSD_ERR_WORKSPACE = 5,      /* workspace missing, misaligned or too small   */

@@ -24,7 +24,7 @@ COMMON = [
 # operation exactly as written (no contraction into fma).
 SOURCES = {
     "abi.hip": [],
-    "attn_fwd.hip": [],
+    "attn_fwd.hip": ["-fno-honor-nans"],
     "qk_prep.hip": ["-ffp-contract=off"],
 }
 

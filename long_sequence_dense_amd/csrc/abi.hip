@@ -24,6 +24,10 @@ int launch_status(hipError_t e) { return e == hipSuccess ? LSD_OK : LSD_ERR_LAUN
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// The attention kernels address one head's rows through 32-bit buffer
+// offsets: L * d * 2 bytes must stay below 2^31.
+int check_attn_len(int L) { return L < (1 << 23) ? LSD_OK : LSD_ERR_SHAPE; }
+
 }  // namespace
 
 extern "C" {
@@ -48,6 +52,7 @@ int attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
                   int H, int L, int d, float softmax_scale, void* stream) {
   int st = check_shape(H, L, d);
   if (st != LSD_OK) return st;
+  if ((st = check_attn_len(L)) != LSD_OK) return st;
   if (!q || !k || !v || !o) return LSD_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LSD_ERR_ALIGN;
   if (lse && ((uintptr_t)lse & 3u)) return LSD_ERR_ALIGN;
@@ -83,6 +88,7 @@ int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
                    int d, float softmax_scale, void* stream) {
   int st = check_shape(H, L, d);
   if (st != LSD_OK) return st;
+  if ((st = check_attn_len(L)) != LSD_OK) return st;
   if (!q_codes || !q_scales || !k_codes || !k_scales || !v || !o) return LSD_ERR_NULL;
   if (!aligned16(q_codes) || !aligned16(q_scales) || !aligned16(k_codes) || !aligned16(k_scales) ||
       !aligned16(v) || !aligned16(o))

@@ -19,16 +19,18 @@
 //     index - and V^T is read from the row-major V tile with the gfx950 LDS
 //     transpose read (ds_read_b64_tr_b16), addressed to reproduce that
 //     permutation.
-//   * K and V tiles are double-buffered in LDS (XOR-swizzled rows, no bank
-//     conflicts for the operand reads) and prefetched through registers one
-//     iteration ahead; K runs one tile ahead of V so that the QK^T MFMAs of
-//     tile t+1 are in flight while the softmax of tile t runs on the VALU.
-//     One barrier per tile.
+//   * Software pipeline, per iteration t: the MFMAs of P(t-1) V(t-1) and of
+//     K(t+1) Q^T are issued while the VALU computes the softmax of tile t, so
+//     the matrix cores and the vector ALU work at the same time inside each
+//     wave.  K runs two tiles ahead of the P.V stage, V one tile.
+//   * K and V tiles are double-buffered in LDS with padded rows (bank-conflict
+//     free operand reads at immediate offsets) and prefetched through
+//     registers one iteration ahead.  One barrier per tile.
 //   * Softmax in base 2 with the scale folded into one FMA per score; the
-//     running max is updated lazily: a row is rescaled only when its tile max
-//     exceeds the max in use by more than 2^8, which changes no result (the
-//     same reference max is used for numerator and denominator) and skips the
-//     O rescale on almost every tile.
+//     running max is updated lazily: a row is rescaled only when
+//     its tile max exceeds the max in use by more than 2^8, which changes no
+//     result (numerator and denominator share the reference max) and skips
+//     the O rescale on almost every tile.
 //   * Workgroups are renumbered so that each XCD (own L2) processes a
 //     contiguous range of query tiles of one head, which then stream the same
 //     K/V tiles at about the same time.
@@ -44,6 +46,8 @@ namespace {
 constexpr int BR = 256;                 // query rows per workgroup
 constexpr int BC = 64;                  // keys per tile
 constexpr int NTHREADS = 512;           // 8 waves
+constexpr int KS = kHeadDim + 8;        // K row stride in LDS (bf16): 272 B
+constexpr int VS = kHeadDim + 32;       // V row stride in LDS (bf16): 320 B
 constexpr float kLazyRescale = 8.0f;    // log2 of the growth allowed before a rescale
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -66,55 +70,73 @@ struct AttnParams {
 };
 
 struct Smem {
-  uint16_t k[2][BC * kHeadDim];         // [key][channel], 16-byte chunks XOR-swizzled by key & 15
-  uint16_t v[2][BC * kHeadDim];         // [key][channel], 16-byte chunks XOR-swizzled by 4*(key & 3)
+  uint16_t k[2][BC * KS];
+  uint16_t v[2][BC * VS];
 };
 
-__device__ __forceinline__ int k_elem(int key, int chunk) { return key * kHeadDim + ((chunk ^ (key & 15)) << 3); }
-__device__ __forceinline__ int v_elem(int key, int chunk) { return key * kHeadDim + ((chunk ^ ((key & 3) << 2)) << 3); }
+// Two FP4 codes (byte J of w) decoded exactly by the hardware (unit scale),
+// times the block scale s.
+template <int J>
+__device__ __forceinline__ void fp4_pair(uint32_t w, float s, float* f) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, J);
+  f[2 * J] = a[0] * s;
+  f[2 * J + 1] = a[1] * s;
+}
+
+// 8 codes (one dword, low nibble first) times scale s -> 8 BF16 bit patterns.
+// Every product E2M1 x E4M3 has at most 6 significant bits and lies in
+// [2^-10, 2688], so the float32 product is exact and truncating it to BF16 is
+// exact.
+__device__ __forceinline__ u16x8 dequant8(uint32_t w, float s) {
+  float f[8];
+  fp4_pair<0>(w, s, f);
+  fp4_pair<1>(w, s, f);
+  fp4_pair<2>(w, s, f);
+  fp4_pair<3>(w, s, f);
+  u16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (uint16_t)(__float_as_uint(f[j]) >> 16);
+  return r;
+}
 
 // 16 NVFP4 values (8 code bytes + 1 scale byte) to 16 BF16 bit patterns.
-// Every product E2M1 x E4M3 has at most 6 significant bits and lies in
-// [2^-10, 2688], so truncating its float32 bits to BF16 is exact.
 __device__ __forceinline__ void dequant16(uint64_t codes, uint32_t scale_byte, u16x8& lo, u16x8& hi) {
   const float s = e4m3_to_f32(scale_byte);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float a = __uint_as_float(e2m1_to_f32_bits((uint32_t)(codes >> (4 * j)) & 0xF)) * s;
-    const float b = __uint_as_float(e2m1_to_f32_bits((uint32_t)(codes >> (4 * (j + 8))) & 0xF)) * s;
-    lo[j] = (uint16_t)(__float_as_uint(a) >> 16);
-    hi[j] = (uint16_t)(__float_as_uint(b) >> 16);
-  }
+  lo = dequant8((uint32_t)codes, s);
+  hi = dequant8((uint32_t)(codes >> 32), s);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
-// Registers holding one prefetched tile slice of this thread.
+// Raw buffer resources over one head's rows: loads past the end of the head
+// return zeros (hardware range check), so ragged last tiles need no branches.
+struct HeadBufs {
+  __amdgpu_buffer_rsrc_t k, v, kc, ks;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One thread's share of a prefetched K tile.
 struct KPrefetch {
-  u16x8 c[2];          // BF16: two 16-byte chunks
-  uint64_t codes;      // FP4: one 16-channel block
+  u32x4 c[2];          // BF16: two 16-byte chunks
+  u32x2 codes;         // FP4: one 16-channel block
   uint32_t scale;
 };
 
 template <bool FP4>
-__device__ __forceinline__ void load_k(const AttnParams& p, size_t head_row0, int kv0, int tid, KPrefetch& r) {
-  const int L = p.L;
+__device__ __forceinline__ void load_k(const HeadBufs& hb, int kv0, int tid, KPrefetch& r) {
   if constexpr (!FP4) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int id = tid + NTHREADS * i;
-      const int key = id >> 4, chunk = id & 15;
-      r.c[i] = (kv0 + key < L) ? *(const u16x8*)(p.k + (head_row0 + kv0 + key) * kHeadDim + chunk * 8) : (u16x8)0;
+      const int id = tid + NTHREADS * i;          // key id >> 4, 16-byte chunk id & 15
+      r.c[i] = __builtin_amdgcn_raw_buffer_load_b128(hb.k, id * 16, kv0 * (kHeadDim * 2), 0);
     }
   } else {
-    const int key = tid >> 3, b = tid & 7;
-    r.codes = 0;
-    r.scale = 0;
-    if (kv0 + key < L) {
-      const size_t row = head_row0 + kv0 + key;
-      r.codes = *(const uint64_t*)(p.kc + row * (kHeadDim / 2) + 8 * b);
-      r.scale = p.ks[row * (kHeadDim / kBlock) + b];
-    }
+    // key tid >> 3, block tid & 7: 8 code bytes and 1 scale byte
+    r.codes = __builtin_amdgcn_raw_buffer_load_b64(hb.kc, tid * 8, kv0 * (kHeadDim / 2), 0);
+    r.scale = __builtin_amdgcn_raw_buffer_load_b8(hb.ks, tid, kv0 * (kHeadDim / kBlock), 0);
   }
 }
 
@@ -124,45 +146,178 @@ __device__ __forceinline__ void store_k(uint16_t* kb, int tid, const KPrefetch& 
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int id = tid + NTHREADS * i;
-      *(u16x8*)(kb + k_elem(id >> 4, id & 15)) = r.c[i];
+      *(u32x4*)(kb + (id >> 4) * KS + (id & 15) * 8) = r.c[i];
     }
   } else {
     const int key = tid >> 3, b = tid & 7;
     u16x8 lo, hi;
-    dequant16(r.codes, r.scale, lo, hi);
-    *(u16x8*)(kb + k_elem(key, 2 * b)) = lo;
-    *(u16x8*)(kb + k_elem(key, 2 * b + 1)) = hi;
+    dequant16(((uint64_t)r.codes[1] << 32) | r.codes[0], r.scale & 0xFF, lo, hi);
+    *(u16x8*)(kb + key * KS + 16 * b) = lo;
+    *(u16x8*)(kb + key * KS + 16 * b + 8) = hi;
   }
 }
 
-__device__ __forceinline__ void load_v(const AttnParams& p, size_t head_row0, int kv0, int tid, u16x8 (&r)[2]) {
+__device__ __forceinline__ void load_v(const HeadBufs& hb, int kv0, int tid, u32x4 (&r)[2]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int id = tid + NTHREADS * i;
-    const int key = id >> 4, chunk = id & 15;
-    r[i] = (kv0 + key < p.L) ? *(const u16x8*)(p.v + (head_row0 + kv0 + key) * kHeadDim + chunk * 8) : (u16x8)0;
+    r[i] = __builtin_amdgcn_raw_buffer_load_b128(hb.v, id * 16, kv0 * (kHeadDim * 2), 0);
   }
 }
 
-__device__ __forceinline__ void store_v(uint16_t* vb, int tid, const u16x8 (&r)[2]) {
+__device__ __forceinline__ void store_v(uint16_t* vb, int tid, const u32x4 (&r)[2]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int id = tid + NTHREADS * i;
-    *(u16x8*)(vb + v_elem(id >> 4, id & 15)) = r[i];
+    *(u32x4*)(vb + (id >> 4) * VS + (id & 15) * 8) = r[i];
   }
 }
 
-// S^T (64 keys x 32 queries) for this wave from one K tile.
-__device__ __forceinline__ void qk_tile(const uint16_t* kb, const bf16x8 (&qreg)[8], int l32, int hf, f32x16 (&s)[2]) {
+// S^T (64 keys x 32 queries) of this wave from one K tile.  kl points at
+// this lane's row (lane % 32) and channel half (8 * (lane / 32)).
+__device__ __forceinline__ void qk_tile(const uint16_t* kl, const bf16x8 (&qreg)[8], f32x16 (&s)[2]) {
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     s[b] = (f32x16)0.0f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u16x8*)(kb + k_elem(32 * b + l32, 2 * kk + hf)));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u16x8*)(kl + 32 * b * KS + 16 * kk));
       s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[b], 0, 0, 0);
     }
   }
+}
+
+// O^T += V^T P^T for one tile.  vl points at this lane's transpose-read
+// address for key chunk 0 and channel block 0: key 4*(lane/32) + (lane%16)/4,
+// channel 16*((lane/16)%2) + 4*(lane%4).
+__device__ __forceinline__ void pv_tile(const uint16_t* vl, const bf16x8 (&pb)[4], f32x16 (&oacc)[4]) {
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const uint16_t* a0 = vl + 16 * cc * VS + 32 * db;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u16*)a0);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u16*)(a0 + 8 * VS));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], oacc[db], 0, 0, 0);
+    }
+  }
+}
+
+// Per-wave running state of the pipeline.
+struct WaveState {
+  bf16x8 qreg[8];                       // Q rows as B operands (8 chunks of 16 channels)
+  f32x16 s[2];                          // S^T of the tile being softmaxed (then of the next tile)
+  f32x16 oacc[4];                       // O^T accumulators, 4 blocks of 32 channels
+  bf16x8 p_prev[4];                     // P^T of the previous tile (B operands)
+  float m_used;                         // reference max (base-2 scaled units) of this lane's row
+  float l_run;                          // this lane's partial row sum (its half of the keys)
+  float alpha;                          // pending O rescale factor (1 = none)
+  bool rescale;                         // wave-uniform: an O rescale is pending
+};
+
+struct Ctx {
+  HeadBufs hb;
+  int tid, hf, k_lane, v_lane, L;
+  float c;                              // softmax scale * log2(e)
+};
+
+// Masks for the scheduling groups: VALU 0x2, MFMA 0x8, VMEM read 0x20,
+// DS read 0x100, DS write 0x200.
+// Operand reads run four MFMAs ahead of their MFMA.
+__device__ __forceinline__ void schedule_pv_half() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+  }
+}
+__device__ __forceinline__ void schedule_qk_half() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+}
+
+// One pipeline iteration t.  First half: P(t-1) V(t-1) on the matrix cores
+// while the VALU exponentiates tile t.  Second half: S(t+1) = K(t+1) Q^T on
+// the matrix cores (into the registers the exponentials just freed) while the
+// VALU finishes the row sums; then V(t) and K(t+2) are staged into LDS.
+template <bool FP4, bool FIRST, bool NEXT, bool NEXT2, bool LAST>
+__device__ __forceinline__ void step(Smem& sm, WaveState& st, const Ctx& cx, int t) {
+  const int kv0 = t * BC;
+  if (st.rescale) {                     // P(t-2) V(t-2) has accumulated; P(t-1) used the new max
+#pragma unroll
+    for (int db = 0; db < 4; ++db) st.oacc[db] *= st.alpha;
+  }
+  KPrefetch kr;
+  u32x4 vr[2];
+  load_v(cx.hb, kv0, cx.tid, vr);
+  if constexpr (NEXT2) load_k<FP4>(cx.hb, kv0 + 2 * BC, cx.tid, kr);
+
+  // ---- first half ----
+  if constexpr (!FIRST) pv_tile(sm.v[(t - 1) & 1] + cx.v_lane, st.p_prev, st.oacc);
+  if constexpr (LAST) {
+    if (kv0 + BC > cx.L) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kv0 + 32 * b + 8 * (i >> 2) + 4 * cx.hf + (i & 3) >= cx.L) st.s[b][i] = -__builtin_inff();
+    }
+  }
+  float m4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    m4[j] = __builtin_fmaxf(__builtin_fmaxf(st.s[j >> 1][8 * (j & 1)], st.s[j >> 1][8 * (j & 1) + 1]),
+                            st.s[j >> 1][8 * (j & 1) + 2]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 3; i < 8; i += 2)
+      m4[j] = __builtin_fmaxf(__builtin_fmaxf(m4[j], st.s[j >> 1][8 * (j & 1) + i]),
+                              i + 1 < 8 ? st.s[j >> 1][8 * (j & 1) + i + 1] : m4[j]);
+  float mx = __builtin_fmaxf(__builtin_fmaxf(m4[0], m4[1]), __builtin_fmaxf(m4[2], m4[3]));
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+    mx = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+  }
+  const float mz = mx * cx.c;
+  st.rescale = __builtin_amdgcn_ballot_w64(mz > st.m_used + kLazyRescale) != 0;
+  const float m_new = st.rescale ? __builtin_fmaxf(st.m_used, mz) : st.m_used;
+  st.alpha = __builtin_amdgcn_exp2f(st.m_used - m_new);
+  st.m_used = m_new;
+  const float negm = -m_new;
+  bf16x8 p_cur[4];
+  float lsum = 0.0f;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    f32x8 pf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[cc >> 1][8 * (cc & 1) + i], cx.c, negm));
+      lsum += pf[i];
+    }
+    p_cur[cc] = __builtin_convertvector(pf, bf16x8);
+  }
+  if constexpr (!FIRST) schedule_pv_half();
+
+  // ---- second half ----
+  if constexpr (NEXT) qk_tile(sm.k[(t + 1) & 1] + cx.k_lane, st.qreg, st.s);
+  st.l_run = st.l_run * st.alpha + lsum;
+  if constexpr (NEXT) schedule_qk_half();
+
+  // ---- stage the prefetched tiles, then one barrier ----
+  store_v(sm.v[t & 1], cx.tid, vr);
+  if constexpr (NEXT2) store_k<FP4>(sm.k[t & 1], cx.tid, kr);
+  __syncthreads();
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) st.p_prev[cc] = p_cur[cc];
 }
 
 template <bool FP4>
@@ -174,7 +329,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hf = lane >> 5;             // which half of the wave
-  const int grp = lane >> 4;            // 16-lane group (transpose reads)
   const int r16 = lane & 15;
 
   // XCD-aware renumbering: hardware block b runs on XCD b % 8; give XCD x a
@@ -189,16 +343,31 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
   const int L = p.L;
   const size_t head_row0 = (size_t)h * (size_t)L;
 
+  Ctx cx;
+  if constexpr (!FP4) {
+    cx.hb.k = head_rsrc(p.k + head_row0 * kHeadDim, (size_t)L * kHeadDim * 2);
+  } else {
+    cx.hb.kc = head_rsrc(p.kc + head_row0 * (kHeadDim / 2), (size_t)L * (kHeadDim / 2));
+    cx.hb.ks = head_rsrc(p.ks + head_row0 * (kHeadDim / kBlock), (size_t)L * (kHeadDim / kBlock));
+  }
+  cx.hb.v = head_rsrc(p.v + head_row0 * kHeadDim, (size_t)L * kHeadDim * 2);
+  cx.tid = tid;
+  cx.hf = hf;
+  cx.L = L;
+  cx.k_lane = l32 * KS + 8 * hf;                                                     // qk_tile operand
+  cx.v_lane = (4 * hf + (r16 >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (r16 & 3);   // pv_tile operand
+  cx.c = p.scale_log2;
+
+  WaveState st;
   // ---- this wave's 32 query rows -> B operands (8 chunks of 16 channels) ----
   const int qrow = qt * BR + wave * 32 + l32;
   const bool qvalid = qrow < L;
-  bf16x8 qreg[8];
   if constexpr (!FP4) {
     const uint16_t* qp = p.q + (head_row0 + (size_t)(qvalid ? qrow : 0)) * kHeadDim + 8 * hf;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       u16x8 t = qvalid ? *(const u16x8*)(qp + 16 * kk) : (u16x8)0;
-      qreg[kk] = __builtin_bit_cast(bf16x8, t);
+      st.qreg[kk] = __builtin_bit_cast(bf16x8, t);
     }
   } else {
     const size_t r = head_row0 + (size_t)(qvalid ? qrow : 0);
@@ -209,123 +378,54 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
       // channels 16kk + 8hf .. +7 live in code bytes 8kk + 4hf .. +3
       const uint32_t c4 = qvalid ? *(const uint32_t*)(cp + 8 * kk + 4 * hf) : 0u;
       const float s = e4m3_to_f32(qvalid ? sp[kk] : 0u);
-      u16x8 t;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float val = __uint_as_float(e2m1_to_f32_bits((c4 >> (4 * j)) & 0xF)) * s;
-        t[j] = (uint16_t)(__float_as_uint(val) >> 16);
-      }
-      qreg[kk] = __builtin_bit_cast(bf16x8, t);
+      st.qreg[kk] = __builtin_bit_cast(bf16x8, dequant8(c4, s));
     }
   }
 
   const int ntiles = (L + BC - 1) / BC;
 
-  // ---- prologue: K(0), V(0), K(1) into LDS; S(0) ----
+  // ---- prologue: K(0), K(1) into LDS; S(0) ----
   {
     KPrefetch kr;
-    u16x8 vr[2];
-    load_k<FP4>(p, head_row0, 0, tid, kr);
-    load_v(p, head_row0, 0, tid, vr);
+    load_k<FP4>(cx.hb, 0, tid, kr);
     store_k<FP4>(sm.k[0], tid, kr);
-    store_v(sm.v[0], tid, vr);
-    if (ntiles > 1) {
-      load_k<FP4>(p, head_row0, BC, tid, kr);
-      store_k<FP4>(sm.k[1], tid, kr);
-    }
+    load_k<FP4>(cx.hb, BC, tid, kr);    // zeros when there is no second tile
+    store_k<FP4>(sm.k[1], tid, kr);
   }
   __syncthreads();
+  qk_tile(sm.k[0] + cx.k_lane, st.qreg, st.s);
+  __syncthreads();                      // K(0)'s buffer is refilled with K(2) in the first iteration
 
-  f32x16 s_cur[2], s_nxt[2];
-  qk_tile(sm.k[0], qreg, l32, hf, s_cur);
-  __syncthreads();                      // K(0)'s buffer is overwritten with K(2) in the first iteration
+#pragma unroll
+  for (int db = 0; db < 4; ++db) st.oacc[db] = (f32x16)0.0f;
+  st.m_used = -__builtin_inff();
+  st.l_run = 0.0f;
+  st.alpha = 1.0f;
+  st.rescale = false;
 
-  f32x16 oacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = (f32x16)0.0f;
-  float m_used = -__builtin_inff();     // reference max (base-2 scaled units) of this lane's row
-  float l_run = 0.0f;                   // this lane's partial row sum (its half of the keys)
-  const float c = p.scale_log2;
-
-  for (int t = 0; t < ntiles; ++t) {
-    const bool has_next = t + 1 < ntiles;
-    const bool has_next2 = t + 2 < ntiles;
-    // prefetch V(t+1) and K(t+2) into registers
-    KPrefetch kr;
-    u16x8 vr[2];
-    if (has_next) load_v(p, head_row0, (t + 1) * BC, tid, vr);
-    if (has_next2) load_k<FP4>(p, head_row0, (t + 2) * BC, tid, kr);
-
-    // S(t+1) on the matrix cores while the softmax of tile t runs
-    if (has_next) qk_tile(sm.k[(t + 1) & 1], qreg, l32, hf, s_nxt);
-
-    // ---- softmax of tile t; lane holds keys 32b + 8(i/4) + 4hf + i%4 ----
-    const int kv0 = t * BC;
-    if (kv0 + BC > L) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kv0 + 32 * b + 8 * (i >> 2) + 4 * hf + (i & 3) >= L) s_cur[b][i] = -__builtin_inff();
-    }
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s_cur[b][i], s_cur[b][i + 1]));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-    const float mz = mx * c;
-    if (__builtin_amdgcn_ballot_w64(mz > m_used + kLazyRescale)) {
-      const float m_new = __builtin_fmaxf(m_used, mz);
-      const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-      m_used = m_new;
-    }
-    const float negm = -m_used;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      f32x8 pf;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[cc >> 1][8 * (cc & 1) + i], c, negm));
-        pf[i] = e;
-        l_run += e;
-      }
-      pb[cc] = __builtin_convertvector(pf, bf16x8);
-    }
-
-    // ---- O^T += V^T P^T: 4 chunks of 16 keys x 4 blocks of 32 channels ----
-    const uint16_t* vb = sm.v[t & 1];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int key0 = 16 * cc + 4 * hf + (r16 >> 2);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int ch = 32 * db + 16 * (grp & 1) + 4 * (r16 & 3);
-        const int e0 = v_elem(key0, ch >> 3) + (ch & 7);
-        const int e1 = v_elem(key0 + 8, ch >> 3) + (ch & 7);
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_u16*)vb + e0));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_u16*)vb + e1));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], oacc[db], 0, 0, 0);
-      }
-    }
-
-    // ---- stage the prefetched tiles, then one barrier ----
-    if (has_next) store_v(sm.v[(t + 1) & 1], tid, vr);
-    if (has_next2) store_k<FP4>(sm.k[t & 1], tid, kr);
-    __syncthreads();
-    if (has_next) {
-      s_cur[0] = s_nxt[0];
-      s_cur[1] = s_nxt[1];
-    }
+  if (ntiles == 1) {
+    step<FP4, true, false, false, true>(sm, st, cx, 0);
+  } else if (ntiles == 2) {
+    step<FP4, true, true, false, false>(sm, st, cx, 0);
+    step<FP4, false, false, false, true>(sm, st, cx, 1);
+  } else {
+    step<FP4, true, true, true, false>(sm, st, cx, 0);
+    for (int t = 1; t < ntiles - 2; ++t) step<FP4, false, true, true, false>(sm, st, cx, t);
+    step<FP4, false, true, false, false>(sm, st, cx, ntiles - 2);
+    step<FP4, false, false, false, true>(sm, st, cx, ntiles - 1);
   }
+  if (st.rescale) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) st.oacc[db] *= st.alpha;
+  }
+  pv_tile(sm.v[(ntiles - 1) & 1] + cx.v_lane, st.p_prev, st.oacc);
 
   // ---- epilogue: O = O / l, BF16 round to nearest even; LSE in natural log ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  float l_tot;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(st.l_run), __float_as_int(st.l_run), false, false);
+    l_tot = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+  }
   const float inv = 1.0f / l_tot;
   if (qvalid) {
     uint16_t* orow = p.o + (head_row0 + qrow) * kHeadDim;
@@ -335,12 +435,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
       for (int g = 0; g < 4; ++g) {
         u16x4 w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = f32_to_bf16_rne(oacc[db][4 * g + j] * inv);
+        for (int j = 0; j < 4; ++j) w[j] = f32_to_bf16_rne(st.oacc[db][4 * g + j] * inv);
         *(u16x4*)(orow + 32 * db + 8 * g + 4 * hf) = w;
       }
     }
     if (p.lse != nullptr && hf == 0)
-      p.lse[head_row0 + qrow] = (m_used + __log2f(l_tot)) * 0.69314718055994530942f;
+      p.lse[head_row0 + qrow] = (st.m_used + __log2f(l_tot)) * 0.69314718055994530942f;
   }
 }
 

@@ -61,6 +61,7 @@ def test_attn_bf16_argument_errors(lib):
     assert f(A, A, A, A, N, 0, 16, 128, 0.1, N) == 2           # H
     assert f(A, A, A, A, N, 2, 0, 128, 0.1, N) == 2            # L
     assert f(A, A, A, A, N, 70000, 70000, 128, 0.1, N) == 2    # H*L overflow
+    assert f(A, A, A, A, N, 1, 1 << 23, 128, 0.1, N) == 2      # one head too long for 32-bit offsets
     assert f(N, A, A, A, N, 2, 16, 128, 0.1, N) == 1           # null q
     assert f(A, A, A, N, N, 2, 16, 128, 0.1, N) == 1           # null o
     assert f(A, B, A, A, N, 2, 16, 128, 0.1, N) == 4           # misaligned k
