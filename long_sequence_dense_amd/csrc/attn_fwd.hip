@@ -43,12 +43,19 @@
 namespace lsd {
 namespace {
 
-constexpr int BR = 256;                 // query rows per workgroup
+#ifndef LSD_ATTN_WAVES
+#define LSD_ATTN_WAVES 8
+#endif
+constexpr int NWAVES = LSD_ATTN_WAVES;  // waves per workgroup, 32 query rows each
+constexpr int BR = 32 * NWAVES;         // query rows per workgroup
 constexpr int BC = 64;                  // keys per tile
-constexpr int NTHREADS = 512;           // 8 waves
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int KCHUNKS = BC * kHeadDim * 2 / 16;   // 16-byte chunks per BF16 tile
+constexpr int NLD = KCHUNKS / NTHREADS;            // chunks per thread per tile
+constexpr int NLD4 = BC * (kHeadDim / kBlock) / NTHREADS;   // FP4 blocks per thread per tile
 constexpr int KS = kHeadDim + 8;        // K row stride in LDS (bf16): 272 B
 constexpr int VS = kHeadDim + 32;       // V row stride in LDS (bf16): 320 B
-constexpr float kLazyRescale = 8.0f;    // log2 of the growth allowed before a rescale
+constexpr float kSumBound = 65536.0f;   // largest per-lane tile sum accepted without recomputing the max
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -120,23 +127,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, si
 
 // One thread's share of a prefetched K tile.
 struct KPrefetch {
-  u32x4 c[2];          // BF16: two 16-byte chunks
-  u32x2 codes;         // FP4: one 16-channel block
-  uint32_t scale;
+  u32x4 c[NLD];        // BF16: 16-byte chunks
+  u32x2 codes[NLD4];   // FP4: 16-channel blocks
+  uint32_t scale[NLD4];
 };
 
 template <bool FP4>
 __device__ __forceinline__ void load_k(const HeadBufs& hb, int kv0, int tid, KPrefetch& r) {
   if constexpr (!FP4) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NLD; ++i) {
       const int id = tid + NTHREADS * i;          // key id >> 4, 16-byte chunk id & 15
       r.c[i] = __builtin_amdgcn_raw_buffer_load_b128(hb.k, id * 16, kv0 * (kHeadDim * 2), 0);
     }
   } else {
-    // key tid >> 3, block tid & 7: 8 code bytes and 1 scale byte
-    r.codes = __builtin_amdgcn_raw_buffer_load_b64(hb.kc, tid * 8, kv0 * (kHeadDim / 2), 0);
-    r.scale = __builtin_amdgcn_raw_buffer_load_b8(hb.ks, tid, kv0 * (kHeadDim / kBlock), 0);
+#pragma unroll
+    for (int i = 0; i < NLD4; ++i) {
+      // key id >> 3, block id & 7: 8 code bytes and 1 scale byte
+      const int id = tid + NTHREADS * i;
+      r.codes[i] = __builtin_amdgcn_raw_buffer_load_b64(hb.kc, id * 8, kv0 * (kHeadDim / 2), 0);
+      r.scale[i] = __builtin_amdgcn_raw_buffer_load_b8(hb.ks, id, kv0 * (kHeadDim / kBlock), 0);
+    }
   }
 }
 
@@ -144,30 +155,34 @@ template <bool FP4>
 __device__ __forceinline__ void store_k(uint16_t* kb, int tid, const KPrefetch& r) {
   if constexpr (!FP4) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NLD; ++i) {
       const int id = tid + NTHREADS * i;
       *(u32x4*)(kb + (id >> 4) * KS + (id & 15) * 8) = r.c[i];
     }
   } else {
-    const int key = tid >> 3, b = tid & 7;
-    u16x8 lo, hi;
-    dequant16(((uint64_t)r.codes[1] << 32) | r.codes[0], r.scale & 0xFF, lo, hi);
-    *(u16x8*)(kb + key * KS + 16 * b) = lo;
-    *(u16x8*)(kb + key * KS + 16 * b + 8) = hi;
+#pragma unroll
+    for (int i = 0; i < NLD4; ++i) {
+      const int id = tid + NTHREADS * i;
+      const int key = id >> 3, b = id & 7;
+      u16x8 lo, hi;
+      dequant16(((uint64_t)r.codes[i][1] << 32) | r.codes[i][0], r.scale[i] & 0xFF, lo, hi);
+      *(u16x8*)(kb + key * KS + 16 * b) = lo;
+      *(u16x8*)(kb + key * KS + 16 * b + 8) = hi;
+    }
   }
 }
 
-__device__ __forceinline__ void load_v(const HeadBufs& hb, int kv0, int tid, u32x4 (&r)[2]) {
+__device__ __forceinline__ void load_v(const HeadBufs& hb, int kv0, int tid, u32x4 (&r)[NLD]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NLD; ++i) {
     const int id = tid + NTHREADS * i;
     r[i] = __builtin_amdgcn_raw_buffer_load_b128(hb.v, id * 16, kv0 * (kHeadDim * 2), 0);
   }
 }
 
-__device__ __forceinline__ void store_v(uint16_t* vb, int tid, const u32x4 (&r)[2]) {
+__device__ __forceinline__ void store_v(uint16_t* vb, int tid, const u32x4 (&r)[NLD]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NLD; ++i) {
     const int id = tid + NTHREADS * i;
     *(u32x4*)(vb + (id >> 4) * VS + (id & 15) * 8) = r[i];
   }
@@ -244,6 +259,23 @@ __device__ __forceinline__ void schedule_qk_half() {
   }
 }
 
+// Exponentials of the tile against the reference max in use, their BF16
+// operands and the lane's partial sum.
+__device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float c, float negm, bf16x8 (&p)[4]) {
+  float lsum = 0.0f;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    f32x8 pf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc >> 1][8 * (cc & 1) + i], c, negm));
+      lsum += pf[i];
+    }
+    p[cc] = __builtin_convertvector(pf, bf16x8);
+  }
+  return lsum;
+}
+
 // One pipeline iteration t.  First half: P(t-1) V(t-1) on the matrix cores
 // while the VALU exponentiates tile t.  Second half: S(t+1) = K(t+1) Q^T on
 // the matrix cores (into the registers the exponentials just freed) while the
@@ -256,7 +288,7 @@ __device__ __forceinline__ void step(Smem& sm, WaveState& st, const Ctx& cx, int
     for (int db = 0; db < 4; ++db) st.oacc[db] *= st.alpha;
   }
   KPrefetch kr;
-  u32x4 vr[2];
+  u32x4 vr[NLD];
   load_v(cx.hb, kv0, cx.tid, vr);
   if constexpr (NEXT2) load_k<FP4>(cx.hb, kv0 + 2 * BC, cx.tid, kr);
 
@@ -271,45 +303,33 @@ __device__ __forceinline__ void step(Smem& sm, WaveState& st, const Ctx& cx, int
           if (kv0 + 32 * b + 8 * (i >> 2) + 4 * cx.hf + (i & 3) >= cx.L) st.s[b][i] = -__builtin_inff();
     }
   }
-  float m4[4];
+  // Exponentials against the reference max in use; a tile whose partial
+  // sum could overflow (above 2^16, infinite on the first tile) is redone
+  // below against its true max.
+  bf16x8 p_cur[4];
+  float lsum = exp_tile(st.s, cx.c, -st.m_used, p_cur);
+  if constexpr (!FIRST) schedule_pv_half();
+
+  // ---- rare path: recompute the tile against its true max ----
+  st.rescale = __builtin_amdgcn_ballot_w64(!(lsum <= kSumBound)) != 0;
+  if (st.rescale) {
+    float mx = -__builtin_inff();
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    m4[j] = __builtin_fmaxf(__builtin_fmaxf(st.s[j >> 1][8 * (j & 1)], st.s[j >> 1][8 * (j & 1) + 1]),
-                            st.s[j >> 1][8 * (j & 1) + 2]);
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 3; i < 8; i += 2)
-      m4[j] = __builtin_fmaxf(__builtin_fmaxf(m4[j], st.s[j >> 1][8 * (j & 1) + i]),
-                              i + 1 < 8 ? st.s[j >> 1][8 * (j & 1) + i + 1] : m4[j]);
-  float mx = __builtin_fmaxf(__builtin_fmaxf(m4[0], m4[1]), __builtin_fmaxf(m4[2], m4[3]));
-  {
+      for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, st.s[b][i]);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
     mx = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+    const float m_new = __builtin_fmaxf(st.m_used, mx * cx.c);
+    st.alpha = __builtin_amdgcn_exp2f(st.m_used - m_new);
+    st.l_run *= st.alpha;
+    st.m_used = m_new;
+    lsum = exp_tile(st.s, cx.c, -m_new, p_cur);
   }
-  const float mz = mx * cx.c;
-  st.rescale = __builtin_amdgcn_ballot_w64(mz > st.m_used + kLazyRescale) != 0;
-  const float m_new = st.rescale ? __builtin_fmaxf(st.m_used, mz) : st.m_used;
-  st.alpha = __builtin_amdgcn_exp2f(st.m_used - m_new);
-  st.m_used = m_new;
-  const float negm = -m_new;
-  bf16x8 p_cur[4];
-  float lsum = 0.0f;
-#pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    f32x8 pf;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[cc >> 1][8 * (cc & 1) + i], cx.c, negm));
-      lsum += pf[i];
-    }
-    p_cur[cc] = __builtin_convertvector(pf, bf16x8);
-  }
-  if constexpr (!FIRST) schedule_pv_half();
+  st.l_run += lsum;
 
   // ---- second half ----
   if constexpr (NEXT) qk_tile(sm.k[(t + 1) & 1] + cx.k_lane, st.qreg, st.s);
-  st.l_run = st.l_run * st.alpha + lsum;
   if constexpr (NEXT) schedule_qk_half();
 
   // ---- stage the prefetched tiles, then one barrier ----
@@ -398,7 +418,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
 
 #pragma unroll
   for (int db = 0; db < 4; ++db) st.oacc[db] = (f32x16)0.0f;
-  st.m_used = -__builtin_inff();
+  st.m_used = -3.402823466e38f;        // finite: the first tile overflows the sum bound and sets the max
   st.l_run = 0.0f;
   st.alpha = 1.0f;
   st.rescale = false;
