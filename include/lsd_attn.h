@@ -82,8 +82,8 @@ int attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 /*
  * Bytes of device workspace qk_prep_fp4 needs for this shape (0 on a bad
- * shape).  It holds exact per-(head, channel, exponent) integer partial sums
- * of K.
+ * shape): H * 128 * ceil(L / 4096) * 16 * 8.  It holds exact fp64 partial
+ * column sums of K.
  */
 size_t qk_prep_fp4_workspace_bytes(int H, int L, int d);
 

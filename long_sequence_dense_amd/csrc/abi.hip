@@ -64,7 +64,7 @@ int attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
 
 size_t qk_prep_fp4_workspace_bytes(int H, int L, int d) {
   if (check_shape(H, L, d) != LSD_OK) return 0;
-  return lsd::prep_workspace_bytes(H);
+  return lsd::prep_workspace_bytes(H, L);
 }
 
 int qk_prep_fp4(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8_t* q_scales,
@@ -76,7 +76,7 @@ int qk_prep_fp4(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8_t*
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_codes) || !aligned16(q_scales) ||
       !aligned16(k_codes) || !aligned16(k_scales) || !aligned16(k_mean))
     return LSD_ERR_ALIGN;
-  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lsd::prep_workspace_bytes(H))
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lsd::prep_workspace_bytes(H, L))
     return LSD_ERR_WORKSPACE;
   (void)hipGetLastError();
   return launch_status(lsd::launch_qk_prep(q, k, q_codes, q_scales, k_codes, k_scales, k_mean, workspace,

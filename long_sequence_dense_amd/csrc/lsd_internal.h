@@ -8,7 +8,6 @@ namespace lsd {
 
 constexpr int kHeadDim = 128;
 constexpr int kBlock = 16;          // channels per NVFP4 scale
-constexpr int kExpBins = 256;       // one exact partial sum per BF16 exponent
 
 // attention (attn_fwd.hip)
 hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -19,7 +18,7 @@ hipError_t launch_attn_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t
                              int H, int L, float scale_log2, hipStream_t stream);
 
 // Q/K preparation (qk_prep.hip)
-size_t prep_workspace_bytes(int H);
+size_t prep_workspace_bytes(int H, int L);
 hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uint8_t* qs,
                           uint8_t* kc, uint8_t* ks, float* kmean, void* ws, int H, int L,
                           hipStream_t stream);

@@ -11,160 +11,76 @@
 // written, so the codes are an exact function of the inputs.
 //
 // Kernels (in launch order):
-//   zero_ws      clear the integer workspace (a fill kernel, graph-safe).
-//   kmean_bins   exact column sums of K: each BF16 value is +-M * 2^(E-134)
-//                with an 8-bit integer M, so per (channel, exponent E) an
-//                integer sum of +-M is exact; LDS int32 bins per workgroup,
-//                flushed into int64 bins [H][128][256] with integer atomics
-//                (order-independent, hence deterministic).
-//   kmean_final  one thread per (head, channel): combine the 256 bins into a
-//                320-bit two's-complement integer, round it once to fp64
-//                (nearest, ties to even), divide by L in fp64 and round to
-//                fp32.
-//   nvfp4_quant  four lanes per 128-channel row, 32 consecutive channels per
-//                lane: (K only) subtract the mean; butterfly stages 0-4 in
-//                registers, stages 5-6 across the lane quad (DPP); multiply by
-//                RN32(1/sqrt(128)); per 16-channel block the E4M3 scale; codes
-//                via a correctly rounded quotient y/s and the hardware
-//                E2M1 conversion with a unit (power-of-two) scale.
+//   quant (Q)        four lanes per 128-channel row, 32 consecutive channels
+//                    per lane: butterfly stages 0-4 in registers, stages 5-6
+//                    across the lane quad (DPP); times RN32(1/sqrt(128)); per
+//                    16-channel block the E4M3 scale (a candidate from
+//                    max|y| * (1/6), settled exactly against the two
+//                    neighbouring rounding boundaries); codes from the correctly rounded
+//                    quotient y/s (Markstein's correction from y * RN(1/s))
+//                    and the hardware E2M1 conversion with a unit
+//                    (power-of-two) scale.
+//   kmean_partial    exact partial column sums of K in fp64: a thread sums up
+//                    to 256 BF16 values per channel; all of them are multiples
+//                    of 2^(E_min-134) and below 2^(E_max-126), so the fp64 sum
+//                    is exact when E_max - E_min <= 37 (tracked per thread
+//                    with packed 16-bit min/max); otherwise the partial is
+//                    flagged and recomputed exactly by kmean_final.
+//   kmean_final      one wave per (head, channel): adds the exact partials
+//                    into 320-bit two's-complement integers (units of
+//                    2^-133), combines them, rounds once to fp64 (nearest,
+//                    ties to even), divides by L in fp64 and rounds to fp32.
+//   quant (K)        as for Q after x = RN32(k - mean).
 #include "lsd_internal.h"
 #include "device_common.h"
 
 namespace lsd {
 namespace {
 
-constexpr int BIN_STRIDE = kExpBins + 1;        // padded LDS row of bins (bank spread)
-constexpr int MEAN_THREADS = 256;
-constexpr int QUANT_THREADS = 256;              // 64 rows per workgroup
+constexpr int QUANT_THREADS = 256;              // 64 rows per iteration
+constexpr int MEAN_THREADS = QUANT_THREADS;     // 16 row slots x 16 channel groups (shares a grid)
+constexpr int MEAN_ROWS = 4096;                 // rows per column-sum workgroup
+constexpr int MEAN_SLOTS = MEAN_THREADS / 16;   // partials per channel per workgroup
 constexpr float kHadamardScale = 0x1.6a09e6p-4f;   // RN32(1/sqrt(128)), bits 0x3DB504F3
 
-__global__ __launch_bounds__(256) void zero_ws_kernel(unsigned long long* __restrict__ ws, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    ws[i] = 0ull;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+int mean_chunks(int L) { return (L + MEAN_ROWS - 1) / MEAN_ROWS; }
+
+// ---------------------------------------------------------------- quantizer --
+
+__device__ __forceinline__ float e4m3_pos(uint32_t j) {            // value of code j, 0 <= j <= 126
+  const uint32_t e = j >> 3, m = j & 7;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * (1.0f / 512.0f);
 }
 
-__global__ __launch_bounds__(MEAN_THREADS) void kmean_bins_kernel(const uint16_t* __restrict__ k,
-                                                                  unsigned long long* __restrict__ bins,
-                                                                  int L, int rows_per_block) {
-  __shared__ int sb[kHeadDim * BIN_STRIDE];
-  const int h = blockIdx.y;
-  const int r0 = blockIdx.x * rows_per_block;
-  const int r1 = min(L, r0 + rows_per_block);
-  for (int i = threadIdx.x; i < kHeadDim * BIN_STRIDE; i += MEAN_THREADS) sb[i] = 0;
-  __syncthreads();
-  const uint16_t* base = k + (size_t)h * (size_t)L * kHeadDim;
-  const int nchunks = (r1 - r0) * (kHeadDim / 8);
-  for (int id = threadIdx.x; id < nchunks; id += MEAN_THREADS) {
-    const int row = r0 + (id >> 4);
-    const int c0 = (id & 15) * 8;
-    const u16x8 v = *(const u16x8*)(base + (size_t)row * kHeadDim + c0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t b = v[j];
-      uint32_t e = (b >> 7) & 0xFF;
-      uint32_t m = b & 0x7F;
-      if (e) m |= 0x80; else e = 1;             // subnormal: M * 2^(1-134)
-      if (m) atomicAdd(&sb[(c0 + j) * BIN_STRIDE + e], (b & 0x8000) ? -(int)m : (int)m);
-    }
-  }
-  __syncthreads();
-  unsigned long long* gb = bins + (size_t)h * kHeadDim * kExpBins;
-  for (int i = threadIdx.x; i < kHeadDim * kExpBins; i += MEAN_THREADS) {
-    const int v = sb[(i >> 8) * BIN_STRIDE + (i & 255)];
-    if (v) atomicAdd(&gb[i], (unsigned long long)(long long)v);
-  }
-}
-
-// value = sum_e bins[e] * 2^(e - 134) exactly, as a multiple of 2^-133 held in
-// 5 little-endian 64-bit limbs (two's complement); then one rounding to fp64.
-__global__ __launch_bounds__(256) void kmean_final_kernel(const unsigned long long* __restrict__ bins,
-                                                          float* __restrict__ kmean, int n, int L) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const long long* b = (const long long*)(bins + (size_t)i * kExpBins);
-  uint64_t limb[5] = {0, 0, 0, 0, 0};
-  for (int e = 1; e < 255; ++e) {
-    const long long B = b[e];
-    if (B == 0) continue;
-    const int sh = e - 1;
-    const int w = sh >> 6, r = sh & 63;
-    const uint64_t ext = B < 0 ? ~0ull : 0ull;
-    const uint64_t lo = (uint64_t)B << r;
-    const uint64_t hi = r ? (uint64_t)(B >> (64 - r)) : ext;
-    uint64_t carry = 0;
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      const uint64_t add = j < w ? 0ull : (j == w ? lo : (j == w + 1 ? hi : ext));
-      const uint64_t s1 = limb[j] + add;
-      const uint64_t c1 = s1 < add;
-      const uint64_t s2 = s1 + carry;
-      const uint64_t c2 = s2 < s1;
-      limb[j] = s2;
-      carry = c1 | c2;
-    }
-  }
-  const bool neg = (long long)limb[4] < 0;
-  if (neg) {
-    uint64_t carry = 1;
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      const uint64_t x = ~limb[j] + carry;
-      carry = (carry && x == 0) ? 1ull : 0ull;
-      limb[j] = x;
-    }
-  }
-  int top = -1;
-#pragma unroll
-  for (int j = 4; j >= 0; --j) {
-    if (top < 0 && limb[j] != 0) top = 64 * j + 63 - __clzll(limb[j]);
-  }
-  double value = 0.0;
-  if (top >= 0) {
-    // bits [pos, pos+64) of the magnitude
-    auto window = [&](int pos) -> uint64_t {
-      const int w = pos >> 6, r = pos & 63;
-      uint64_t x = w < 5 ? (limb[w] >> r) : 0ull;
-      if (r && w + 1 < 5) x |= limb[w + 1] << (64 - r);
-      return x;
-    };
-    if (top <= 52) {
-      value = __builtin_ldexp((double)limb[0], -133);           // exact
-    } else {
-      int shift = top - 52;
-      uint64_t m = window(shift) & ((1ull << 53) - 1);
-      const bool guard = (window(shift - 1) & 1ull) != 0;
-      bool sticky = false;
-      for (int j = 0; j < 5 && !sticky; ++j) {
-        const int lo_bit = 64 * j;
-        if (lo_bit >= shift - 1) break;
-        const int nb = (shift - 1) - lo_bit;                     // bits of this limb below the guard
-        const uint64_t mask = nb >= 64 ? ~0ull : ((1ull << nb) - 1);
-        sticky = (limb[j] & mask) != 0;
-      }
-      if (guard && (sticky || (m & 1ull))) ++m;
-      if (m >> 53) { m >>= 1; ++shift; }
-      value = __builtin_ldexp((double)m, shift - 133);
-    }
-    if (neg) value = -value;
-  }
-  kmean[i] = (float)(value / (double)L);
-}
-
-// Nearest E4M3 code to amax / 6 (amax >= 0), ties to even, saturating at 448.
-// r = RN32(amax / 6) (one fp64 division, then one rounding to fp32) is never
-// pushed onto an E4M3 rounding boundary unless amax / 6 is exactly on it, so
-// rounding r to 3 mantissa bits equals rounding amax / 6 itself.
+// Nearest E4M3 code to amax/6 (ties to the even code, saturating at 448).
+// Candidate: round r = RN(amax * RN(1/6)) (within a few units in the last
+// place of amax/6) to 3 mantissa bits; then settle it exactly against the
+// values of max|y| where the nearest scale changes, 6 * (v_{c-1} + v_c) / 2 and
+// 6 * (v_c + v_{c+1}) / 2 (at most 7 significant bits: exact in fp32), which
+// moves it by at most one.
 __device__ __forceinline__ uint32_t e4m3_scale_code(float amax) {
-  const float r = (float)((double)amax / 6.0);
-  if (!(r < 448.0f)) return 0x7Eu;
-  if (r >= 0x1p-6f) {
+  const float r = amax * 0x1.555556p-3f;
+  uint32_t c;
+  if (!(r < 448.0f)) {
+    c = 0x7Eu;
+  } else if (r >= 0x1p-6f) {
     const uint32_t u = __float_as_uint(r);
-    const uint32_t rounded = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;   // exponent|3-bit mantissa, RNE
-    return rounded - (120u << 3);
+    c = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+    c = c > 0x7Eu ? 0x7Eu : c;
+  } else {
+    c = (uint32_t)__builtin_rintf(r * 512.0f);
   }
-  return (uint32_t)__builtin_rintf(r * 512.0f);                        // subnormal m * 2^-9, m in 0..8
+  const float v = e4m3_pos(c);
+  const float hi = c < 0x7Eu ? 3.0f * (v + e4m3_pos(c + 1)) : __builtin_inff();
+  const float lo = c > 0u ? 3.0f * (e4m3_pos(c - 1) + v) : -1.0f;
+  if (amax > hi || (amax == hi && (c & 1u))) return c + 1;          // a tie goes to the even neighbour
+  if (amax < lo || (amax == lo && (c & 1u))) return c - 1;
+  return c;
 }
 
+// Partner value across the lane quad: lane ^ 1 and lane ^ 2.
 __device__ __forceinline__ float dpp_xor1(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
@@ -172,11 +88,14 @@ __device__ __forceinline__ float dpp_xor2(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
 }
 
-__global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_kernel(const uint16_t* __restrict__ src,
-                                                                    const float* __restrict__ kmean,
-                                                                    uint8_t* __restrict__ codes,
-                                                                    uint8_t* __restrict__ scales,
-                                                                    long long nrows, int L) {
+// Four lanes per 128-channel row, 32 consecutive channels per lane.  grid:
+// one lane quad per row of all heads.  K (KMEAN): x = RN32(k - mean) first.
+template <bool KMEAN>
+__global__ __launch_bounds__(QUANT_THREADS) void quant_kernel(const uint16_t* __restrict__ src,
+                                                              const float* __restrict__ kmean,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales, long long nrows,
+                                                              int L) {
   const int tid = threadIdx.x;
   const int part = tid & 3;                      // channels 32*part .. 32*part+31
   const long long row = (long long)blockIdx.x * (QUANT_THREADS / 4) + (tid >> 2);
@@ -186,11 +105,14 @@ __global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_kernel(const uint16
   float x[32];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u16x8 raw = *(const u16x8*)(rp + 8 * i);
+    const u32x4 raw = *(const u32x4*)(rp + 8 * i);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[8 * i + j] = bf16_bits_to_f32(raw[j]);
+    for (int j = 0; j < 4; ++j) {
+      x[8 * i + 2 * j] = __uint_as_float(raw[j] << 16);
+      x[8 * i + 2 * j + 1] = __uint_as_float(raw[j] & 0xFFFF0000u);
+    }
   }
-  if (kmean != nullptr) {
+  if constexpr (KMEAN) {
     const float* km = kmean + (row / L) * kHeadDim + part * 32;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -212,43 +134,45 @@ __global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_kernel(const uint16
       }
     }
   }
-  // stages 5 and 6: channel bits 5 and 6 are bits 0 and 1 of the lane in its quad.
-  // The lane with the bit clear holds x_i and forms x_i + x_j; its partner holds
-  // x_j and forms x_i - x_j; fma(own, +-1, partner) is that one rounded operation.
-  const float sg5 = (part & 1) ? -1.0f : 1.0f;
+  // stages 5 and 6: channel bits 5 and 6 are bits 0 and 1 of the lane in its
+  // quad.  The lane with the bit clear holds x_i and forms x_i + x_j; its
+  // partner holds x_j and forms x_i - x_j; fma(own, +-1, partner) is that one
+  // rounded operation, signed zeros included.
+  const float k5 = (part & 1) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], sg5, dpp_xor1(x[i]));
-  const float sg6 = (part & 2) ? -1.0f : 1.0f;
+  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], k5, dpp_xor1(x[i]));
+  const float k6 = (part & 2) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], sg6, dpp_xor2(x[i]));
-
+  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], k6, dpp_xor2(x[i]));
 #pragma unroll
   for (int i = 0; i < 32; ++i) x[i] = x[i] * kHadamardScale;
 
   uint32_t scode[2];
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
+  for (int blk2 = 0; blk2 < 2; ++blk2) {
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(x[16 * blk + i]));
+    for (int i = 0; i < 16; i += 2)
+      amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(x[16 * blk2 + i]),
+                                                   __builtin_fabsf(x[16 * blk2 + i + 1])));
     const uint32_t sc = e4m3_scale_code(amax);
-    scode[blk] = sc;
-    const float s = e4m3_to_f32(sc);
-    const float rinv = sc ? (float)(1.0 / (double)s) : 0.0f;    // RN32(1/s)
+    scode[blk2] = sc;
+    const float s = e4m3_pos(sc);
+    const float rinv = sc ? (float)(1.0 / (double)s) : 0.0f;     // RN32(1/s)
     // t = RN32(y / s): Markstein's correction from q0 = RN(y * RN(1/s)); the
     // remainder fma(q0, s, -y) is exact.  Written so that t keeps the sign of
-    // y also when y is a signed zero, and t = +-0 when s = 0.
+    // y also when y is a signed zero, and t = +-0 when s = 0 (rinv = 0).
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float y = x[16 * blk + i];
+      const float y = x[16 * blk2 + i];
       const float q0 = y * rinv;
       const float rr = __builtin_fmaf(q0, s, -y);
-      x[16 * blk + i] = __builtin_fmaf(-rr, rinv, q0);
+      x[16 * blk2 + i] = __builtin_fmaf(-rr, rinv, q0);
     }
   }
   // E2M1 with round-to-nearest-even and saturation (unit scale): channel 2j in
   // the low nibble of byte j, 2j+1 in the high nibble.
+  u32x4 wv;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     uint32_t acc = 0u;
@@ -256,36 +180,220 @@ __global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_kernel(const uint16
     acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, x[8 * d + 2], x[8 * d + 3], 1.0f, 1);
     acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, x[8 * d + 4], x[8 * d + 5], 1.0f, 2);
     acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, x[8 * d + 6], x[8 * d + 7], 1.0f, 3);
-    w[d] = acc;
+    wv[d] = acc;
   }
-  u32x4 wv = {w[0], w[1], w[2], w[3]};
   *(u32x4*)(codes + row * (kHeadDim / 2) + part * 16) = wv;
   *(uint16_t*)(scales + row * (kHeadDim / kBlock) + part * 2) = (uint16_t)(scode[0] | (scode[1] << 8));
 }
 
+// ---------------------------------------------------------------- mean -------
+
+// Exact partial column sums of rows chunk*4096 .. +4095 of head h.  Thread t:
+// channels 8*(t%16) .. +7, rows r0 + t/16 + 16*i.
+__device__ __forceinline__ void mean_block(const uint16_t* __restrict__ k, double* __restrict__ parts, int L,
+                                           int nparts, int h, int chunk) {
+  const int tid = threadIdx.x;
+  const int g = tid & 15, slot = tid >> 4;
+  const int r0 = chunk * MEAN_ROWS;
+  const int r1 = min(L, r0 + MEAN_ROWS);
+  const uint16_t* base = k + (size_t)h * (size_t)L * kHeadDim + 8 * g;
+  double acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0;
+  u16x2 emax = {0, 0};                          // max magnitude bits (sign cleared)
+  u16x2 emin = {0xFFFF, 0xFFFF};                // min of (magnitude bits - 1): zero never wins
+  for (int r = r0 + slot; r < r1; r += 4 * MEAN_SLOTS) {
+    u32x4 w[4];                                  // four rows in flight; rows past the end add zero
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[u] = r + u * MEAN_SLOTS < r1 ? *(const u32x4*)(base + (size_t)(r + u * MEAN_SLOTS) * kHeadDim) : (u32x4)0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += (double)__uint_as_float(w[u][j] << 16);
+        acc[2 * j + 1] += (double)__uint_as_float(w[u][j] & 0xFFFF0000u);
+        const u16x2 mag = __builtin_bit_cast(u16x2, w[u][j] & 0x7FFF7FFFu);
+        emax = __builtin_elementwise_max(emax, mag);
+        emin = __builtin_elementwise_min(emin, mag - (u16x2){1, 1});
+      }
+    }
+  }
+  const uint32_t mx = emax[0] > emax[1] ? emax[0] : emax[1];
+  const uint32_t mn = emin[0] < emin[1] ? emin[0] : emin[1];
+  bool exact = true;
+  if (mn != 0xFFFFu) {                           // some nonzero value
+    const int e_max = (int)(mx >> 7);
+    int e_min = (int)((mn + 1) >> 7);
+    e_min = e_min < 1 ? 1 : e_min;               // subnormals share exponent 1's quantum
+    exact = e_max - e_min <= 37;                 // at most 256 values per partial
+  }
+  double* out = parts + ((size_t)h * kHeadDim + 8 * g) * nparts + (size_t)chunk * MEAN_SLOTS + slot;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[(size_t)j * nparts] = exact ? acc[j] : __builtin_nan("");
+}
+
+// 320-bit two's-complement accumulator in units of 2^-133.
+struct BigSum {
+  uint64_t limb[5];
+  __device__ void clear() {
+#pragma unroll
+    for (int j = 0; j < 5; ++j) limb[j] = 0;
+  }
+  // += B * 2^sh for a signed 64-bit B and 0 <= sh < 256.
+  __device__ void add_shifted(long long B, int sh) {
+    const int w = sh >> 6, r = sh & 63;
+    const uint64_t ext = B < 0 ? ~0ull : 0ull;
+    const uint64_t lo = (uint64_t)B << r;
+    const uint64_t hi = r ? (uint64_t)(B >> (64 - r)) : ext;
+    uint64_t carry = 0;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const uint64_t add = j < w ? 0ull : (j == w ? lo : (j == w + 1 ? hi : ext));
+      const uint64_t s1 = limb[j] + add;
+      const uint64_t c1 = s1 < add;
+      const uint64_t s2 = s1 + carry;
+      const uint64_t c2 = s2 < s1;
+      limb[j] = s2;
+      carry = c1 | c2;
+    }
+  }
+  // += one BF16 value, exactly: +-M * 2^(E-134), subnormals as E = 1.
+  __device__ void add_bf16(uint32_t b) {
+    uint32_t e = (b >> 7) & 0xFF;
+    uint32_t m = b & 0x7F;
+    if (e) m |= 0x80; else e = 1;
+    if (m) add_shifted((b & 0x8000) ? -(long long)m : (long long)m, (int)e - 1);
+  }
+  // += an fp64 value that is an exact multiple of 2^-133.
+  __device__ void add_f64(double d) {
+    const uint64_t bits = __double_as_longlong(d);
+    const int e = (int)((bits >> 52) & 0x7FF);
+    if (e == 0) return;                          // zero (no nonzero multiple of 2^-133 is this small)
+    const long long m = (long long)((bits & ((1ull << 52) - 1)) | (1ull << 52));
+    const long long sm = (bits >> 63) ? -m : m;
+    const int sh = e - 1075 + 133;               // value = m * 2^(e-1075)
+    if (sh >= 0) add_shifted(sm, sh);
+    else add_shifted(sm >> (-sh), 0);            // the dropped bits are zero
+  }
+  // RN64 of the sum.
+  __device__ double round_f64() {
+    const bool neg = (long long)limb[4] < 0;
+    uint64_t mag[5];
+    uint64_t carry = neg ? 1ull : 0ull;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const uint64_t x = neg ? ~limb[j] + carry : limb[j];
+      carry = (neg && carry && x == 0) ? 1ull : 0ull;
+      mag[j] = x;
+    }
+    int top = -1;
+#pragma unroll
+    for (int j = 4; j >= 0; --j)
+      if (top < 0 && mag[j] != 0) top = 64 * j + 63 - __clzll(mag[j]);
+    if (top < 0) return 0.0;
+    auto window = [&](int pos) -> uint64_t {                     // bits [pos, pos + 64)
+      const int w = pos >> 6, r = pos & 63;
+      uint64_t x = w < 5 ? (mag[w] >> r) : 0ull;
+      if (r && w + 1 < 5) x |= mag[w + 1] << (64 - r);
+      return x;
+    };
+    double v;
+    if (top <= 52) {
+      v = __builtin_ldexp((double)mag[0], -133);                 // exact
+    } else {
+      int shift = top - 52;
+      uint64_t m = window(shift) & ((1ull << 53) - 1);
+      const bool guard = (window(shift - 1) & 1ull) != 0;
+      bool sticky = false;
+      for (int j = 0; j < 5 && !sticky; ++j) {
+        const int lo_bit = 64 * j;
+        if (lo_bit >= shift - 1) break;
+        const int nb = (shift - 1) - lo_bit;                     // bits of this limb below the guard bit
+        const uint64_t mask = nb >= 64 ? ~0ull : ((1ull << nb) - 1);
+        sticky = (mag[j] & mask) != 0;
+      }
+      if (guard && (sticky || (m & 1ull))) ++m;
+      if (m >> 53) { m >>= 1; ++shift; }
+      v = __builtin_ldexp((double)m, shift - 133);
+    }
+    return neg ? -v : v;
+  }
+};
+
+// One wave per (head, channel): each lane adds its share of the partials into
+// its own 320-bit integer, then lane 0 adds the 64 integers (exact).
+constexpr int FINAL_THREADS = 64;
+
+__global__ __launch_bounds__(FINAL_THREADS) void kmean_final_kernel(const uint16_t* __restrict__ k,
+                                                                    const double* __restrict__ parts,
+                                                                    float* __restrict__ kmean, int L, int nparts) {
+  __shared__ uint64_t limbs[FINAL_THREADS][5];
+  const int i = blockIdx.x;                                     // head * 128 + channel
+  const int h = i / kHeadDim, c = i - h * kHeadDim;
+  const int lane = threadIdx.x;
+  const double* p = parts + (size_t)i * nparts;
+  BigSum acc;
+  acc.clear();
+  for (int j = lane; j < nparts; j += FINAL_THREADS) {
+    const double d = p[j];
+    if (d == d) {
+      acc.add_f64(d);
+    } else {                                     // flagged: recompute this partial's values exactly
+      const int chunk = j / MEAN_SLOTS, slot = j - chunk * MEAN_SLOTS;
+      const int r1 = min(L, (chunk + 1) * MEAN_ROWS);
+      const uint16_t* col = k + (size_t)h * (size_t)L * kHeadDim + c;
+      for (int r = chunk * MEAN_ROWS + slot; r < r1; r += MEAN_SLOTS) acc.add_bf16(col[(size_t)r * kHeadDim]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 5; ++j) limbs[lane][j] = acc.limb[j];
+  __syncthreads();
+  if (lane == 0) {
+    for (int t = 1; t < FINAL_THREADS; ++t) {
+      uint64_t carry = 0;
+#pragma unroll
+      for (int j = 0; j < 5; ++j) {
+        const uint64_t add = limbs[t][j];
+        const uint64_t s1 = acc.limb[j] + add;
+        const uint64_t c1 = s1 < add;
+        const uint64_t s2 = s1 + carry;
+        const uint64_t c2 = s2 < s1;
+        acc.limb[j] = s2;
+        carry = c1 | c2;
+      }
+    }
+    kmean[i] = (float)(acc.round_f64() / (double)L);
+  }
+}
+
+// The K column sums.  grid (chunks, H).
+__global__ __launch_bounds__(MEAN_THREADS) void kmean_partial_kernel(const uint16_t* __restrict__ k,
+                                                                     double* __restrict__ parts, int L,
+                                                                     int nparts) {
+  mean_block(k, parts, L, nparts, (int)blockIdx.y, (int)blockIdx.x);
+}
+
 }  // namespace
 
-size_t prep_workspace_bytes(int H) { return (size_t)H * kHeadDim * kExpBins * sizeof(unsigned long long); }
+size_t prep_workspace_bytes(int H, int L) {
+  return (size_t)H * kHeadDim * (size_t)mean_chunks(L) * MEAN_SLOTS * sizeof(double);
+}
 
 hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uint8_t* qs, uint8_t* kc,
                           uint8_t* ks, float* kmean, void* ws, int H, int L, hipStream_t stream) {
-  unsigned long long* bins = (unsigned long long*)ws;
-  const size_t nbins = (size_t)H * kHeadDim * kExpBins;
-  hipLaunchKernelGGL(zero_ws_kernel, dim3(512), dim3(256), 0, stream, bins, nbins);
-  // about two LDS-heavy workgroups per CU in total
-  const int blocks_per_head = max(1, min((L + 255) / 256, (512 + H - 1) / H));
-  const int rows_per_block = (L + blocks_per_head - 1) / blocks_per_head;
-  const int nbx = (L + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL(kmean_bins_kernel, dim3(nbx, H), dim3(MEAN_THREADS), 0, stream, k, bins, L,
-                     rows_per_block);
-  const int n = H * kHeadDim;
-  hipLaunchKernelGGL(kmean_final_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, bins, kmean, n, L);
+  double* parts = (double*)ws;
+  const int nchunks = mean_chunks(L);
+  const int nparts = nchunks * MEAN_SLOTS;
   const long long nrows = (long long)H * L;
   const unsigned qblocks = (unsigned)((nrows + (QUANT_THREADS / 4) - 1) / (QUANT_THREADS / 4));
-  hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(qblocks), dim3(QUANT_THREADS), 0, stream, q,
-                     (const float*)nullptr, qc, qs, nrows, L);
-  hipLaunchKernelGGL(nvfp4_quant_kernel, dim3(qblocks), dim3(QUANT_THREADS), 0, stream, k,
-                     (const float*)kmean, kc, ks, nrows, L);
+  hipLaunchKernelGGL(quant_kernel<false>, dim3(qblocks), dim3(QUANT_THREADS), 0, stream, q, (const float*)nullptr,
+                     qc, qs, nrows, L);
+  hipLaunchKernelGGL(kmean_partial_kernel, dim3(nchunks, H), dim3(MEAN_THREADS), 0, stream, k, parts, L, nparts);
+  hipLaunchKernelGGL(kmean_final_kernel, dim3(H * kHeadDim), dim3(FINAL_THREADS), 0, stream, k,
+                     (const double*)parts, kmean, L, nparts);
+  hipLaunchKernelGGL(quant_kernel<true>, dim3(qblocks), dim3(QUANT_THREADS), 0, stream, k, (const float*)kmean,
+                     kc, ks, nrows, L);
   return hipGetLastError();
 }
 
