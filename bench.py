@@ -26,6 +26,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense BF16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+COPY_PROBE_BYTES = 1 << 30    # plain copy of known size that calibrates FETCH_SIZE / WRITE_SIZE
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json")
 METRIC = "attention TFLOP/s and % of MFMA peak at 109k tokens, BF16 and FP4-QK paths"
 
 
@@ -55,9 +57,30 @@ def gen_inputs(torch, name):
     return cfg, out
 
 
-def cpu_baseline(H, L, d, seconds_budget=20.0):
-    """Time the CPU oracle (as it stands) on a bounded sample of the workload and
-    extrapolate a full step; returns the cpu_baseline object."""
+def kernel_source_hash():
+    """sha256 of the attention kernel source: counter-derived traffic is only
+    reported for the kernel it was measured on."""
+    import hashlib
+    src = os.path.join(ROOT, "long_sequence_dense_amd", "csrc", "attn_fwd.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+
+
+def stored_traffic():
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except Exception:
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(H, L, d):
+    """Time the CPU oracle (as it stands) on a bounded sample of the workload
+    (about 15 s of CPU work on 16 cores) and extrapolate a full step; returns
+    the cpu_baseline object."""
     from long_sequence_dense_amd import inputs
     from oracle.attention import attention_fp64
     from oracle.nvfp4 import qk_prep_fp4
@@ -68,7 +91,7 @@ def cpu_baseline(H, L, d, seconds_budget=20.0):
         cores = len(os.sched_getaffinity(0))
     cfg = inputs.CONFIGS["clip15s"]
     heads = [0, 1]
-    rows = inputs.sample_rows(L, 384)
+    rows = inputs.sample_rows(L, 12288)
     q = inputs.make_tensor(cfg, "q", heads)
     k = inputs.make_tensor(cfg, "k", heads)
     v = inputs.make_tensor(cfg, "v", heads)
@@ -78,11 +101,13 @@ def cpu_baseline(H, L, d, seconds_budget=20.0):
     t_attn = time.time() - t0
     attn_rate = len(heads) * len(rows) * 4.0 * L * d / t_attn          # FLOP/s
     fcfg = inputs.CONFIGS["fp4"]
-    qf = inputs.make_tensor(fcfg, "q", [0])
-    kf = inputs.make_tensor(fcfg, "k", [0])
+    prep_heads = [0, 1, 2, 3]
+    qf = inputs.make_tensor(fcfg, "q", prep_heads)
+    kf = inputs.make_tensor(fcfg, "k", prep_heads)
     t0 = time.time()
     qk_prep_fp4(qf, kf)
-    t_prep_head = time.time() - t0
+    t_prep = time.time() - t0
+    t_prep_head = t_prep / len(prep_heads)
     full_attn_s = attn_flop(H, L, d) / attn_rate
     step_s = 2 * full_attn_s + H * t_prep_head
     return {
@@ -91,9 +116,10 @@ def cpu_baseline(H, L, d, seconds_budget=20.0):
         "cores": int(cores),
         "kind": "oracle",
         "sample": ("fp64 numpy oracle: BF16 attention for %d query rows x %d heads at L=%d "
-                   "(%.1f s, %.2f GFLOP/s), NVFP4 prep of 1 full head of Q and K (%.1f s); "
+                   "(%.1f s, %.2f GFLOP/s), NVFP4 prep of %d full heads of Q and K (%.1f s); "
                    "full step extrapolated to %.0f s (2 attention calls + %d heads of prep)"
-                   % (len(rows), len(heads), L, t_attn, attn_rate / 1e9, t_prep_head, step_s, H)),
+                   % (len(rows), len(heads), L, t_attn, attn_rate / 1e9, len(prep_heads), t_prep,
+                      step_s, H)),
     }
 
 
@@ -105,6 +131,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "bf16"], default="all",
                     help="bf16: time only attn_fwd_bf16 (for profiling runs)")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="for hardware-counter runs: one %d-byte torch copy (counter calibration), "
+                         "then one launch of each kernel on the benchmark workload; no timing" % COPY_PROBE_BYTES)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -157,6 +186,18 @@ def main():
             ev["prep"].append((b, c))
             ev["fp4"].append((c, e))
 
+    if args.pmc_probe:
+        a = torch.empty(COPY_PROBE_BYTES // 2, dtype=torch.int16, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)                                   # the calibration copy
+        torch.cuda.synchronize()
+        step(False)
+        torch.cuda.synchronize()
+        log("pmc probe done")
+        return
+
     log("warmup %d steps ..." % args.warmup)
     for _ in range(args.warmup):
         step(False)
@@ -192,13 +233,7 @@ def main():
         paths["attn_fwd_fp4qk"] = {"ms": round(t_fp4, 3), "TFLOP/s": round(a4, 1),
                                    "frac_of_peak": round(a4 / PEAK_BF16_TFLOPS, 4),
                                    "mfma_precision": "bf16 (exact dequantization of NVFP4 Q/K)"}
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "attn_fwd_bf16_traffic.json")
-    if os.path.exists(tpath):
-        try:
-            traffic = json.load(open(tpath)).get("hbm_bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = stored_traffic()
     res = {
         "metric": METRIC,
         "value": round(value, 2),
