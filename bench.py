@@ -58,11 +58,15 @@ def gen_inputs(torch, name):
 
 
 def kernel_source_hash():
-    """sha256 of the attention kernel source: counter-derived traffic is only
-    reported for the kernel it was measured on."""
+    """sha256 of the attention kernel source with comments and blank lines
+    removed: counter-derived traffic is only reported for the code it was
+    measured on."""
     import hashlib
+    import re
     src = os.path.join(ROOT, "long_sequence_dense_amd", "csrc", "attn_fwd.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in open(src).read().splitlines())
+    code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()
 
 
 def stored_traffic():

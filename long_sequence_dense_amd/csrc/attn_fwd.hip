@@ -26,11 +26,14 @@
 //   * K and V tiles are double-buffered in LDS with padded rows (bank-conflict
 //     free operand reads at immediate offsets) and prefetched through
 //     registers one iteration ahead.  One barrier per tile.
-//   * Softmax in base 2 with the scale folded into one FMA per score; the
-//     running max is updated lazily: a row is rescaled only when
-//     its tile max exceeds the max in use by more than 2^8, which changes no
-//     result (numerator and denominator share the reference max) and skips
-//     the O rescale on almost every tile.
+//   * Softmax in base 2 with the scale folded into one FMA per score.  The
+//     exponentials of a tile are taken against the reference max already in
+//     use, without computing the tile max first; only when a lane's tile sum
+//     exceeds 2^16 (or overflows, as on the first tile) does the wave compute
+//     the true tile max, rescale its running sum and O, and redo the
+//     exponentials.  Any reference max gives the same result (numerator and
+//     denominator share it); the bound keeps P, the sums and O far from
+//     overflow, and the rare path is taken on a few tiles per row.
 //   * Workgroups are renumbered so that each XCD (own L2) processes a
 //     contiguous range of query tiles of one head, which then stream the same
 //     K/V tiles at about the same time.
