@@ -58,7 +58,11 @@ constexpr int NLD = KCHUNKS / NTHREADS;            // chunks per thread per tile
 constexpr int NLD4 = BC * (kHeadDim / kBlock) / NTHREADS;   // FP4 blocks per thread per tile
 constexpr int KS = kHeadDim + 8;        // K row stride in LDS (bf16): 272 B
 constexpr int VS = kHeadDim + 32;       // V row stride in LDS (bf16): 320 B
-constexpr float kSumBound = 65536.0f;   // largest per-lane tile sum accepted without recomputing the max
+constexpr float kSumBound = 65536.0f;
+#ifndef LSD_ATTN_KPRE
+#define LSD_ATTN_KPRE 4
+#endif
+constexpr int KPRE = LSD_ATTN_KPRE;     // K operands of the next tile read during the P.V half   // largest per-lane tile sum accepted without recomputing the max
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -193,13 +197,21 @@ __device__ __forceinline__ void store_v(uint16_t* vb, int tid, const u32x4 (&r)[
 
 // S^T (64 keys x 32 queries) of this wave from one K tile.  kl points at
 // this lane's row (lane % 32) and channel half (8 * (lane / 32)).
-__device__ __forceinline__ void qk_tile(const uint16_t* kl, const bf16x8 (&qreg)[8], f32x16 (&s)[2]) {
+__device__ __forceinline__ bf16x8 k_operand(const uint16_t* kl, int i) {   // i = 8 * block + chunk
+  return __builtin_bit_cast(bf16x8, *(const u16x8*)(kl + 32 * (i >> 3) * KS + 16 * (i & 7)));
+}
+
+// The first KPRE operands come from registers read earlier (kpre).
+template <int NPRE>
+__device__ __forceinline__ void qk_tile(const uint16_t* kl, const bf16x8 (&kpre)[KPRE], const bf16x8 (&qreg)[8],
+                                        f32x16 (&s)[2]) {
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     s[b] = (f32x16)0.0f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u16x8*)(kl + 32 * b * KS + 16 * kk));
+      const int i = 8 * b + kk;
+      const bf16x8 a = i < NPRE ? kpre[i < KPRE ? i : 0] : k_operand(kl, i);
       s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[b], 0, 0, 0);
     }
   }
@@ -242,22 +254,27 @@ struct Ctx {
 
 // Masks for the scheduling groups: VALU 0x2, MFMA 0x8, VMEM read 0x20,
 // DS read 0x100, DS write 0x200.
-// Operand reads run four MFMAs ahead of their MFMA.
-__device__ __forceinline__ void schedule_pv_half() {
+// V operand reads run four MFMAs ahead of their MFMA; the first KPRE K
+// operands of the next tile are read during the last four P.V MFMAs, so the
+// score MFMAs start with KPRE operands in registers and keep reading KPRE
+// ahead.
+__device__ __forceinline__ void schedule_pv_half(bool kpre) {
   __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    else if (kpre) __builtin_amdgcn_sched_group_barrier(0x100, KPRE / 4, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
   }
 }
 __device__ __forceinline__ void schedule_qk_half() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  if (KPRE < 4) __builtin_amdgcn_sched_group_barrier(0x100, 4 - KPRE, 0);
+  constexpr int AHEAD = KPRE < 4 ? 4 : KPRE;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i + AHEAD < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
   }
 }
@@ -311,7 +328,12 @@ __device__ __forceinline__ void step(Smem& sm, WaveState& st, const Ctx& cx, int
   // below against its true max.
   bf16x8 p_cur[4];
   float lsum = exp_tile(st.s, cx.c, -st.m_used, p_cur);
-  if constexpr (!FIRST) schedule_pv_half();
+  bf16x8 kpre[KPRE];
+  if constexpr (NEXT) {
+#pragma unroll
+    for (int i = 0; i < KPRE; ++i) kpre[i] = k_operand(sm.k[(t + 1) & 1] + cx.k_lane, i);
+  }
+  if constexpr (!FIRST) schedule_pv_half(NEXT);
 
   // ---- rare path: recompute the tile against its true max ----
   st.rescale = __builtin_amdgcn_ballot_w64(!(lsum <= kSumBound)) != 0;
@@ -332,7 +354,7 @@ __device__ __forceinline__ void step(Smem& sm, WaveState& st, const Ctx& cx, int
   st.l_run += lsum;
 
   // ---- second half ----
-  if constexpr (NEXT) qk_tile(sm.k[(t + 1) & 1] + cx.k_lane, st.qreg, st.s);
+  if constexpr (NEXT) qk_tile<KPRE>(sm.k[(t + 1) & 1] + cx.k_lane, kpre, st.qreg, st.s);
   if constexpr (NEXT) schedule_qk_half();
 
   // ---- stage the prefetched tiles, then one barrier ----
@@ -416,7 +438,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
     store_k<FP4>(sm.k[1], tid, kr);
   }
   __syncthreads();
-  qk_tile(sm.k[0] + cx.k_lane, st.qreg, st.s);
+  {
+    bf16x8 none[KPRE];
+    qk_tile<0>(sm.k[0] + cx.k_lane, none, st.qreg, st.s);
+  }
   __syncthreads();                      // K(0)'s buffer is refilled with K(2) in the first iteration
 
 #pragma unroll
