@@ -166,6 +166,34 @@ def make_inputs(name_or_cfg, heads=None, H=None, L=None):
     }
 
 
+# Toy heads of the section "FP4 attention": 64 channels (four 16-value
+# blocks), 32 keys, Gaussian values, one bias per channel shared by every key,
+# two channels scaled up.  The pages give no magnitudes; these are the ones of
+# the long-clip inputs above (bias N(0, variance 2), gain x10 on Q and K) and
+# 32 queries per head.
+TOY_D = 64
+TOY_LEN = 32
+TOY_OUTLIERS = 2
+TOY_GAIN = np.float32(10.0)
+
+
+def toy_heads(n_heads, seed=5):
+    """Q, K, V BF16 bits [n_heads, 32, 64] of the toy heads; per head h the
+    same recipe as above with rng streams (seed, tensor_id, h)."""
+    out = {w: np.empty((n_heads, TOY_LEN, TOY_D), np.uint16) for w in ("q", "k", "v")}
+    for h in range(n_heads):
+        ch = np.sort(_rng(seed, TID_OUTLIER, h).choice(TOY_D, TOY_OUTLIERS, replace=False))
+        off = _rng(seed, TID_OFFSET, h).normal(0.0, math.sqrt(2.0), TOY_D)
+        for w, tid in (("q", TID_Q), ("k", TID_K), ("v", TID_V)):
+            x = _rng(seed, tid, h).standard_normal((TOY_LEN, TOY_D), dtype=np.float32)
+            if w != "v":
+                x[:, ch] *= TOY_GAIN
+            if w == "k":
+                x = (x.astype(np.float64) + off[None, :]).astype(np.float32)
+            out[w][h] = f32_to_bf16_bits(x)
+    return out
+
+
 def sample_rows(L, n_random, seed=12345, tiles=(64, 128, 256)):
     """Query rows for sampled parity at large L: the first and last rows of
     every tile size in ``tiles`` around the start and the ragged end, plus

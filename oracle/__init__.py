@@ -10,7 +10,10 @@ Contents
 ``oracle.attention``  fp64 softmax attention (the plain definition).
 ``oracle.nvfp4``      the Q/K preparation for FP4 attention (mean key, Hadamard
                       rotation, NVFP4 block quantization), the E4M3/E2M1 codecs
-                      and exact dequantization.
+                      and exact dequantization; switches for the ablation
+                      variants (no smoothing, no rotation).
+``oracle.fp4_error``  relative attention error of the FP4-QK variants against
+                      exact attention.
 
 Source: "Pika H3 Flex in FastVideo: 7x Faster, and Near Real Time in 4-bit"
 (haoailab blog), sections "Faster at BF16" and "FP4 attention".  Every function
@@ -25,9 +28,11 @@ from .nvfp4 import (  # noqa: F401
     e4m3_decode_table,
     kmean_exact,
     hadamard_butterfly_fp32,
+    hadamard_scale_f32,
     HADAMARD_SCALE_F32,
     e4m3_scale_code,
     e2m1_codes,
     qk_prep_fp4,
     dequant_nvfp4,
 )
+from .fp4_error import fp4_attention_error, fp4_outputs, relative_error  # noqa: F401

@@ -33,6 +33,15 @@ P6  codes: if s == 0 every code is the signed zero signbit(y)<<3; otherwise the
     index, quotients above 6 saturate to index 7; code = signbit(y)<<3 | e.
 P7  byte j of a row = code[2j] | code[2j+1] << 4; scale byte = E4M3 bits of s.
 
+Ablation variants (same section: quantizing naively costs accuracy, and the
+two exact transforms recover most of it; its table of per-layer errors lists
+plain FP4 above FP4 with smoothed K and the Hadamard rotation).  ``smooth``
+off skips P1-P2 (K is quantized as given and the reported mean is zero);
+``rotate`` off skips P3-P4 (y = x, blocks of consecutive original channels).
+The defaults (both on) are the method.  For the pages' toy heads the row
+length d may also be 64 (four blocks; with the rotation, a 6-stage butterfly
+and RN32(1/sqrt(64)) = 1/8).
+
 Arithmetic: values are held in float64.  Each RN32 is a float64 operation
 followed by a cast to float32.  For +, -, * and / of float32 operands this
 double rounding equals the single IEEE float32 operation because 53 >= 2*24+2
@@ -122,16 +131,25 @@ def kmean_exact(k_head):
     return out
 
 
+def hadamard_scale_f32(n):
+    """P4's constant for rows of length n (a power of two): RN32(1/sqrt(n)).
+    1/sqrt(n) is irrational or a power of two, so rounding its fp64 value to
+    float32 cannot hit a float32 midpoint and equals the direct rounding."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("rotation length must be a power of two")
+    return np.float32(1.0 / math.sqrt(n))
+
+
 def hadamard_butterfly_fp32(x):
-    """P3: in-order Sylvester butterfly over the last axis (length 128) with a
-    float32 rounding after every add and subtract.  ``x`` holds float32 values
-    (any float dtype); returns float32."""
+    """P3: in-order Sylvester butterfly over the last axis (length 128, or
+    another power of two) with a float32 rounding after every add and
+    subtract.  ``x`` holds float32 values (any float dtype); returns float32."""
     x = np.asarray(x, dtype=np.float32).copy()
     n = x.shape[-1]
-    if n != D_HEAD:
-        raise ValueError("butterfly length must be 128")
+    if n < 2 or n & (n - 1):
+        raise ValueError("butterfly length must be a power of two")
     lead = x.shape[:-1]
-    for s in range(7):
+    for s in range(n.bit_length() - 1):
         h = 1 << s
         v = x.reshape(lead + (n // (2 * h), 2, h)).astype(np.float64)
         a = v[..., 0, :]
@@ -176,59 +194,66 @@ def e2m1_codes(y, s):
     return (sign | e).astype(np.uint8)
 
 
-def _quantize_rows(x_f32):
-    """P3-P7 for rows of 128 float32 values; returns (codes [n, 64] u8,
-    scales [n, 8] u8)."""
-    n = x_f32.shape[0]
-    hx = hadamard_butterfly_fp32(x_f32)
-    y = (hx.astype(np.float64) * np.float64(HADAMARD_SCALE_F32)).astype(np.float32)
-    yb = y.reshape(n, D_HEAD // BLOCK, BLOCK)
+def _quantize_rows(x_f32, rotate=True):
+    """P3-P7 (P5-P7 only when ``rotate`` is off) for rows of d float32
+    values; returns (codes [n, d/2] u8, scales [n, d/16] u8)."""
+    n, d = x_f32.shape
+    if rotate:
+        hx = hadamard_butterfly_fp32(x_f32)
+        y = (hx.astype(np.float64) * np.float64(hadamard_scale_f32(d))).astype(np.float32)
+    else:
+        y = np.asarray(x_f32, dtype=np.float32)
+    yb = y.reshape(n, d // BLOCK, BLOCK)
     amax = np.abs(yb).max(axis=-1)
     scode = e4m3_scale_code(amax)
     sval = _E4M3[scode]
-    codes = e2m1_codes(yb, sval).reshape(n, D_HEAD)
+    codes = e2m1_codes(yb, sval).reshape(n, d)
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
     return packed, scode
 
 
-def qk_prep_fp4(q_bits, k_bits, heads=None, rows=None):
+def qk_prep_fp4(q_bits, k_bits, heads=None, rows=None, smooth=True, rotate=True):
     """The full preparation P0-P7 for BF16 Q and K given as uint16 bit arrays
-    [H, L, 128].
+    [H, L, d] (d = 128; 64 for the toy heads).
 
     ``heads``: optional head indices to process (default all); ``rows``:
     optional token-row indices whose codes are returned (the mean always uses
-    every row of K).  Returns a dict with q_codes [h, n, 64], q_scales
-    [h, n, 8], k_codes, k_scales (same shapes) and k_mean [h, 128] float32.
+    every row of K).  ``smooth`` / ``rotate``: the ablation switches of the
+    module header.  Returns a dict with q_codes [h, n, d/2], q_scales
+    [h, n, d/16], k_codes, k_scales (same shapes) and k_mean [h, d] float32.
     """
     q_bits = np.asarray(q_bits)
     k_bits = np.asarray(k_bits)
-    if q_bits.shape != k_bits.shape or q_bits.ndim != 3 or q_bits.shape[2] != D_HEAD:
-        raise ValueError("q and k must both be [H, L, 128]")
-    H, L, _ = q_bits.shape
+    if q_bits.shape != k_bits.shape or q_bits.ndim != 3 or q_bits.shape[2] not in (64, D_HEAD):
+        raise ValueError("q and k must both be [H, L, 128] (or [H, L, 64])")
+    H, L, d = q_bits.shape
     hs = list(range(H)) if heads is None else list(heads)
     ridx = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
     n = ridx.size
     out = {
-        "q_codes": np.empty((len(hs), n, D_HEAD // 2), np.uint8),
-        "q_scales": np.empty((len(hs), n, D_HEAD // BLOCK), np.uint8),
-        "k_codes": np.empty((len(hs), n, D_HEAD // 2), np.uint8),
-        "k_scales": np.empty((len(hs), n, D_HEAD // BLOCK), np.uint8),
-        "k_mean": np.empty((len(hs), D_HEAD), np.float32),
+        "q_codes": np.empty((len(hs), n, d // 2), np.uint8),
+        "q_scales": np.empty((len(hs), n, d // BLOCK), np.uint8),
+        "k_codes": np.empty((len(hs), n, d // 2), np.uint8),
+        "k_scales": np.empty((len(hs), n, d // BLOCK), np.uint8),
+        "k_mean": np.zeros((len(hs), d), np.float32),
     }
     for i, h in enumerate(hs):
-        kh = bf16_bits_to_f64(k_bits[h])
-        kbar = kmean_exact(kh)
-        xk = (kh[ridx] - kbar.astype(np.float64)).astype(np.float32)
+        if smooth:
+            kh = bf16_bits_to_f64(k_bits[h])
+            kbar = kmean_exact(kh)
+            xk = (kh[ridx] - kbar.astype(np.float64)).astype(np.float32)
+            out["k_mean"][i] = kbar
+        else:
+            xk = bf16_bits_to_f64(k_bits[h][ridx]).astype(np.float32)
         xq = bf16_bits_to_f64(q_bits[h][ridx]).astype(np.float32)
-        out["k_mean"][i] = kbar
-        out["q_codes"][i], out["q_scales"][i] = _quantize_rows(xq)
-        out["k_codes"][i], out["k_scales"][i] = _quantize_rows(xk)
+        out["q_codes"][i], out["q_scales"][i] = _quantize_rows(xq, rotate)
+        out["k_codes"][i], out["k_scales"][i] = _quantize_rows(xk, rotate)
     return out
 
 
 def dequant_nvfp4(codes, scales):
-    """Exact real values of packed NVFP4 rows: codes [..., 64] u8 (low nibble
-    = even channel), scales [..., 8] E4M3 bytes.  Returns float64 [..., 128]."""
+    """Exact real values of packed NVFP4 rows: codes [..., d/2] u8 (low nibble
+    = even channel), scales [..., d/16] E4M3 bytes.  Returns float64 [..., d]."""
     codes = np.asarray(codes, dtype=np.uint8)
     scales = np.asarray(scales, dtype=np.uint8)
     lo = codes & 0xF

@@ -57,3 +57,25 @@ def test_sample_rows():
     assert r.min() >= 0 and r.max() == 108999 and len(set(r)) == len(r)
     for t in (64, 128, 256):
         assert (108999 // t) * t in r
+
+
+def test_toy_heads_structure():
+    t = inputs.toy_heads(8)
+    assert t["q"].shape == (8, 32, 64) and t["k"].shape == (8, 32, 64) and t["v"].shape == (8, 32, 64)
+    again = inputs.toy_heads(8)
+    for w in ("q", "k", "v"):
+        assert np.array_equal(t[w], again[w])
+    assert np.array_equal(inputs.toy_heads(3)["k"], t["k"][:3])        # heads independent of the count
+    q = inputs.bf16_bits_to_f32(t["q"]).astype(np.float64)
+    k = inputs.bf16_bits_to_f32(t["k"]).astype(np.float64)
+    v = inputs.bf16_bits_to_f32(t["v"]).astype(np.float64)
+    for h in range(8):
+        rms_q = np.sqrt((q[h] ** 2).mean(axis=0))
+        big = np.argsort(rms_q)[-2:]
+        assert np.all(rms_q[big] > 4 * np.median(rms_q))                # two scaled-up channels
+        centred = k[h] - k[h].mean(axis=0)
+        assert np.all(np.sqrt((centred[:, big] ** 2).mean(axis=0)) > 4)  # same channels on K
+    # every key of a head shares one bias per channel: the column means of K
+    # spread far more than those of Q (outlier channels aside)
+    assert np.std(k.mean(axis=1)) > 2 * np.std(np.median(q, axis=1))
+    assert abs(np.std(v) - 1.0) < 0.1

@@ -246,6 +246,22 @@ def test_hadamard_scale_is_nearest_float32():
     assert lo * lo < Fraction(1, 128) < hi * hi
 
 
+def test_hadamard_scale_other_lengths():
+    assert nvfp4.hadamard_scale_f32(128) == nvfp4.HADAMARD_SCALE_F32
+    assert nvfp4.hadamard_scale_f32(64) == np.float32(0.125)
+    for n in (2, 4, 16, 32, 64, 128, 256, 1024):
+        assert nvfp4.hadamard_scale_f32(n) == nearest_f32_to_inv_sqrt(n), n
+    with pytest.raises(ValueError):
+        nvfp4.hadamard_scale_f32(96)
+
+
+def test_butterfly_length_64_equals_integer_matrix():
+    rng = np.random.default_rng(37)
+    x = rng.integers(-1024, 1025, (16, 64))
+    got = nvfp4.hadamard_butterfly_fp32(x.astype(np.float32))
+    assert np.array_equal(got.astype(np.int64), x @ sylvester(64))
+
+
 # ---- mean -----------------------------------------------------------------------
 
 def test_mean_exact_against_fraction():
@@ -272,29 +288,52 @@ def test_mean_cancellation_case():
 
 # ---- one whole row by brute force ------------------------------------------------
 
-def brute_prep_rows(xrows):
-    """float32 rows [n, 128] (already mean-subtracted) -> (packed codes, scales)
+def nearest_f32_to_inv_sqrt(n):
+    """RN32(1/sqrt(n)) by exact search: the float32 c with (c - ulp/2)^2 <
+    1/n < (c + ulp/2)^2 (no float arithmetic on the constant)."""
+    target = Fraction(1, n)
+    c = Fraction(float(np.float32(1.0 / math.sqrt(n))))
+    for cand in (c, Fraction(float(next_up(np.float32(c)))), Fraction(float(next_down(np.float32(c))))):
+        e = math.floor(math.log2(float(cand)))
+        ulp = Fraction(2) ** (e - 23)
+        if (cand - ulp / 2) ** 2 <= target <= (cand + ulp / 2) ** 2:
+            return np.float32(cand)
+    raise AssertionError(n)
+
+
+def brute_prep_rows(xrows, rotate=True):
+    """float32 rows [n, d] (already mean-subtracted) -> (packed codes, scales)
     with float32 scalar butterfly and Fraction-argmin rounding, plain loops."""
-    c = np.float32(nvfp4.HADAMARD_SCALE_F32)
+    d = len(xrows[0])
+    c = nearest_f32_to_inv_sqrt(d)
     codes_out, scales_out = [], []
     for row in xrows:
         v = [np.float32(t) for t in row]
-        for s in range(7):
-            h = 1 << s
-            for i in range(128):
-                if i & h == 0:
-                    a, b = v[i], v[i + h]
-                    v[i], v[i + h] = np.float32(a + b), np.float32(a - b)
-        y = [np.float32(t * c) for t in v]
+        if rotate:
+            for s in range(d.bit_length() - 1):
+                h = 1 << s
+                for i in range(d):
+                    if i & h == 0:
+                        a, b = v[i], v[i + h]
+                        v[i], v[i + h] = np.float32(a + b), np.float32(a - b)
+            y = [np.float32(t * c) for t in v]
+        else:
+            y = v
         codes, scales = [], []
-        for b in range(8):
+        for b in range(d // 16):
             blk = y[16 * b:16 * b + 16]
             sc = brute_scale_code(max(abs(t) for t in blk))
             scales.append(sc)
             codes += [brute_e2m1_code(t, E4M3_POS[sc]) for t in blk]
-        codes_out.append([codes[2 * j] | (codes[2 * j + 1] << 4) for j in range(64)])
+        codes_out.append([codes[2 * j] | (codes[2 * j + 1] << 4) for j in range(d // 2)])
         scales_out.append(scales)
     return np.array(codes_out, dtype=np.uint8), np.array(scales_out, dtype=np.uint8)
+
+
+def fraction_mean_f32(kh):
+    L = kh.shape[0]
+    return np.array([np.float32(float(sum(Fraction(float(t)) for t in kh[:, c])) / L)
+                     for c in range(kh.shape[1])], dtype=np.float32)
 
 
 def test_prep_matches_brute_force_rows():
@@ -322,6 +361,94 @@ def test_prep_matches_brute_force_rows():
             bc, bs = brute_prep_rows(x)
             assert np.array_equal(out[name + "_codes"][h], bc), name
             assert np.array_equal(out[name + "_scales"][h], bs), name
+
+
+@pytest.mark.parametrize("smooth,rotate", [(False, False), (True, False), (False, True)])
+def test_prep_variants_match_brute_force_rows(smooth, rotate):
+    # The ablation variants: without smoothing K is quantized as given and the
+    # reported mean is zero; without the rotation the blocks are consecutive
+    # original channels with no 1/sqrt(d) factor.
+    rng = np.random.default_rng(30 + 2 * smooth + rotate)
+    H, L = 2, 12
+    q = rng.standard_t(3, (H, L, 128)).astype(np.float32)
+    k = (rng.standard_t(3, (H, L, 128)) + rng.normal(0, 2, (H, 1, 128))).astype(np.float32)
+    q[:, :, 7] *= 20
+    k[:, :, 7] *= 20
+    q[1, 2] = 0.0
+    qb = (q.view(np.uint32) >> 16).astype(np.uint16)
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+    out = nvfp4.qk_prep_fp4(qb, kb, smooth=smooth, rotate=rotate)
+    for h in range(H):
+        kh = nvfp4.bf16_bits_to_f64(kb[h])
+        if smooth:
+            kbar = fraction_mean_f32(kh)
+            xk = np.array([[np.float32(np.float32(kh[l, c]) - kbar[c]) for c in range(128)]
+                           for l in range(L)], dtype=np.float32)
+        else:
+            kbar = np.zeros(128, np.float32)
+            xk = kh.astype(np.float32)
+        assert np.array_equal(out["k_mean"][h].view(np.uint32), kbar.view(np.uint32))
+        xq = nvfp4.bf16_bits_to_f64(qb[h]).astype(np.float32)
+        for name, x in (("q", xq), ("k", xk)):
+            bc, bs = brute_prep_rows(x, rotate=rotate)
+            assert np.array_equal(out[name + "_codes"][h], bc), name
+            assert np.array_equal(out[name + "_scales"][h], bs), name
+
+
+@pytest.mark.parametrize("smooth,rotate", [(False, False), (True, True)])
+def test_prep_toy_width_matches_brute_force_rows(smooth, rotate):
+    # 64-channel rows (the pages' toy heads): 6-stage butterfly, RN32(1/8).
+    rng = np.random.default_rng(36 + smooth)
+    L = 10
+    q = (rng.standard_normal((1, L, 64)) * 3).astype(np.float32)
+    k = (rng.standard_normal((1, L, 64)) + rng.normal(0, 2, (1, 1, 64))).astype(np.float32)
+    qb = (q.view(np.uint32) >> 16).astype(np.uint16)
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+    out = nvfp4.qk_prep_fp4(qb, kb, smooth=smooth, rotate=rotate)
+    assert out["q_codes"].shape == (1, L, 32) and out["q_scales"].shape == (1, L, 4)
+    kh = nvfp4.bf16_bits_to_f64(kb[0])
+    kbar = fraction_mean_f32(kh) if smooth else np.zeros(64, np.float32)
+    xk = np.array([[np.float32(np.float32(kh[l, c]) - kbar[c]) for c in range(64)] for l in range(L)],
+                  dtype=np.float32)
+    for name, x in (("q", nvfp4.bf16_bits_to_f64(qb[0]).astype(np.float32)), ("k", xk)):
+        bc, bs = brute_prep_rows(x, rotate=rotate)
+        assert np.array_equal(out[name + "_codes"][0], bc), name
+        assert np.array_equal(out[name + "_scales"][0], bs), name
+
+
+def test_smoothing_is_identity_on_zero_mean_keys():
+    # Keys in +- pairs have an exactly zero column mean: smoothing changes
+    # nothing, with or without the rotation; Q never depends on smoothing.
+    rng = np.random.default_rng(38)
+    half = (rng.standard_t(3, (2, 20, 128)) * 4).astype(np.float32)
+    kb = (np.concatenate([half, -half], axis=1).view(np.uint32) >> 16).astype(np.uint16)
+    qb = (rng.standard_t(3, (2, 40, 128)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    for rotate in (False, True):
+        a = nvfp4.qk_prep_fp4(qb, kb, smooth=True, rotate=rotate)
+        b = nvfp4.qk_prep_fp4(qb, kb, smooth=False, rotate=rotate)
+        assert np.all(a["k_mean"] == 0)
+        for key in ("q_codes", "q_scales", "k_codes", "k_scales"):
+            assert np.array_equal(a[key], b[key]), (rotate, key)
+
+
+def test_plain_quantization_is_lossless_on_the_grid():
+    # Blocks made of E2M1 values times one E4M3 scale s, each with an entry
+    # +-6s: the nearest scale to max/6 is s itself and every value is a grid
+    # point, so the plain variant (no smoothing, no rotation) loses nothing.
+    rng = np.random.default_rng(39)
+    e2 = nvfp4.e2m1_decode_table()
+    e4 = nvfp4.e4m3_decode_table()
+    n = 50
+    sc = rng.integers(0x08, 0x76, (n, 8))           # normal scales with headroom
+    cd = rng.integers(0, 16, (n, 128))
+    cd[:, ::16] = rng.choice([7, 15], (n, 8))       # one +-6 per block
+    x = e2[cd] * np.repeat(e4[sc], 16, axis=1)
+    xb = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(nvfp4.bf16_bits_to_f64(xb), x)
+    out = nvfp4.qk_prep_fp4(xb[None], xb[None], smooth=False, rotate=False)
+    for name in ("q", "k"):
+        back = nvfp4.dequant_nvfp4(out[name + "_codes"][0], out[name + "_scales"][0])
+        assert np.array_equal(back, x)
 
 
 def test_rows_and_heads_selection():
