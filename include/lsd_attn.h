@@ -54,11 +54,12 @@ enum lsd_status {
   LSD_ERR_ALIGN = 4,          /* a tensor pointer is not 16-byte aligned      */
   LSD_ERR_WORKSPACE = 5,      /* workspace missing, misaligned or too small   */
   LSD_ERR_LAUNCH = 6,         /* the HIP runtime rejected a kernel launch     */
-  LSD_ERR_SCALE = 7           /* softmax_scale is not finite and positive     */
+  LSD_ERR_SCALE = 7,          /* softmax_scale is not finite and positive     */
+  LSD_ERR_FLAGS = 8           /* unknown bits in a flags argument             */
 };
 
 /* Version of this ABI (the value of LSD_ABI_VERSION the library was built with). */
-#define LSD_ABI_VERSION 1
+#define LSD_ABI_VERSION 2
 int lsd_abi_version(void);
 
 /* Static description of a status code ("ok", "null pointer", ...). */
@@ -115,9 +116,37 @@ int qk_prep_fp4(const uint16_t* q, const uint16_t* k,
                 float* k_mean, void* workspace, size_t workspace_bytes,
                 int H, int L, int d, void* stream);
 
+/* Bits of the `flags` argument of qk_prep_fp4_ex. */
+enum lsd_prep_flags {
+  LSD_PREP_SMOOTH_K = 1,      /* subtract the per-head mean key before quantizing K */
+  LSD_PREP_ROTATE = 2         /* shared 128-point Hadamard rotation of Q and K      */
+};
+
+/*
+ * qk_prep_fp4_ex - qk_prep_fp4 with the two transforms switched separately,
+ * for ablations of the quantization error.
+ *   flags : LSD_PREP_SMOOTH_K | LSD_PREP_ROTATE gives exactly qk_prep_fp4;
+ *           other bits -> LSD_ERR_FLAGS.
+ *   Without LSD_PREP_SMOOTH_K: K is quantized as given (x = k); workspace may
+ *           be NULL (it is not used); k_mean may be NULL, and if it is not it
+ *           is written with zeros (the mean that was subtracted).
+ *   Without LSD_PREP_ROTATE: no butterfly and no 1/sqrt(128) factor; the
+ *           16-channel blocks are consecutive original channels.
+ * Everything else (layouts, rounding, codes, errors) is as in qk_prep_fp4.
+ * Source: "FP4 attention" (quantizing naively costs accuracy; smoothing K and
+ * the Hadamard rotation recover part of it; its per-layer error table).
+ */
+int qk_prep_fp4_ex(const uint16_t* q, const uint16_t* k,
+                   uint8_t* q_codes, uint8_t* q_scales,
+                   uint8_t* k_codes, uint8_t* k_scales,
+                   float* k_mean, void* workspace, size_t workspace_bytes,
+                   int H, int L, int d, int flags, void* stream);
+
 /*
  * attn_fwd_fp4qk - attention on quantized Q and K.
- *   q_codes, q_scales, k_codes, k_scales : as written by qk_prep_fp4.
+ *   q_codes, q_scales, k_codes, k_scales : as written by qk_prep_fp4 (or by
+ *             qk_prep_fp4_ex: any variant, as long as Q and K come from the
+ *             same call).
  *   v   : [H, L, d] BF16 bits.   o : [H, L, d] BF16 bits, written.
  *   lse : optional [H, L] float32 (NULL to skip).
  * Scores are softmax_scale * (Qhat . Khat) where Qhat, Khat are the exact

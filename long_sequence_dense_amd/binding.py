@@ -18,7 +18,10 @@ HEAD_DIM = 128
 STATUS = {
     0: "LSD_OK", 1: "LSD_ERR_NULL", 2: "LSD_ERR_SHAPE", 3: "LSD_ERR_UNSUPPORTED_D",
     4: "LSD_ERR_ALIGN", 5: "LSD_ERR_WORKSPACE", 6: "LSD_ERR_LAUNCH", 7: "LSD_ERR_SCALE",
+    8: "LSD_ERR_FLAGS",
 }
+PREP_SMOOTH_K = 1       # lsd_prep_flags
+PREP_ROTATE = 2
 
 # name -> (restype, argtypes); mirrors include/lsd_attn.h
 _P = ctypes.c_void_p
@@ -31,6 +34,7 @@ SIGNATURES = {
     "attn_fwd_bf16": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
     "qk_prep_fp4_workspace_bytes": (_S, [_I, _I, _I]),
     "qk_prep_fp4": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _P]),
+    "qk_prep_fp4_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _P]),
     "attn_fwd_fp4qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
 }
 
@@ -123,9 +127,7 @@ def qk_prep_fp4_workspace_bytes(H, L, d=HEAD_DIM):
     return int(load_library().qk_prep_fp4_workspace_bytes(H, L, d))
 
 
-def qk_prep_fp4(q, k, out=None, workspace=None, stream=None):
-    """Mean-K, Hadamard and NVFP4 quantization of Q and K ([H, L, 128] BF16).
-    Returns dict(q_codes, q_scales, k_codes, k_scales, k_mean)."""
+def _prep_outputs(q, k, out):
     import torch
     H, L, d = q.shape
     _need(q, "q", _bf16_types(), (H, L, d))
@@ -144,14 +146,42 @@ def qk_prep_fp4(q, k, out=None, workspace=None, stream=None):
     for n in ("q_scales", "k_scales"):
         _need(out[n], n, (torch.uint8,), (H, L, d // 16))
     _need(out["k_mean"], "k_mean", (torch.float32,), (H, d))
+    return out
+
+
+def qk_prep_fp4(q, k, out=None, workspace=None, stream=None):
+    """Mean-K, Hadamard and NVFP4 quantization of Q and K ([H, L, 128] BF16).
+    Returns dict(q_codes, q_scales, k_codes, k_scales, k_mean)."""
+    import torch
+    H, L, d = q.shape
+    out = _prep_outputs(q, k, out)
     need = qk_prep_fp4_workspace_bytes(H, L, d)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = load_library().qk_prep_fp4(
         _ptr(q), _ptr(k), _ptr(out["q_codes"]), _ptr(out["q_scales"]), _ptr(out["k_codes"]),
         _ptr(out["k_scales"]), _ptr(out["k_mean"]), _ptr(workspace),
         workspace.numel() * workspace.element_size(), H, L, d, _stream(stream))
     _check("qk_prep_fp4", st)
+    return out
+
+
+def qk_prep_fp4_ex(q, k, flags, out=None, workspace=None, stream=None):
+    """qk_prep_fp4 with the transforms switched by ``flags`` (PREP_SMOOTH_K |
+    PREP_ROTATE = the full method).  Without smoothing no workspace is used and
+    k_mean is written with zeros."""
+    import torch
+    H, L, d = q.shape
+    out = _prep_outputs(q, k, out)
+    if workspace is None:
+        need = qk_prep_fp4_workspace_bytes(H, L, d) if flags & PREP_SMOOTH_K else 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().qk_prep_fp4_ex(
+        _ptr(q), _ptr(k), _ptr(out["q_codes"]), _ptr(out["q_scales"]), _ptr(out["k_codes"]),
+        _ptr(out["k_scales"]), _ptr(out["k_mean"]), _ptr(workspace), nbytes, H, L, d, int(flags),
+        _stream(stream))
+    _check("qk_prep_fp4_ex", st)
     return out
 
 

@@ -44,6 +44,7 @@ const char* lsd_status_str(int status) {
     case LSD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case LSD_ERR_LAUNCH: return "kernel launch failed";
     case LSD_ERR_SCALE: return "softmax_scale must be finite and > 0";
+    case LSD_ERR_FLAGS: return "unknown flag bits";
     default: return "unknown status";
   }
 }
@@ -67,20 +68,30 @@ size_t qk_prep_fp4_workspace_bytes(int H, int L, int d) {
   return lsd::prep_workspace_bytes(H, L);
 }
 
-int qk_prep_fp4(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8_t* q_scales,
-                uint8_t* k_codes, uint8_t* k_scales, float* k_mean, void* workspace,
-                size_t workspace_bytes, int H, int L, int d, void* stream) {
+int qk_prep_fp4_ex(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8_t* q_scales,
+                   uint8_t* k_codes, uint8_t* k_scales, float* k_mean, void* workspace,
+                   size_t workspace_bytes, int H, int L, int d, int flags, void* stream) {
   int st = check_shape(H, L, d);
   if (st != LSD_OK) return st;
-  if (!q || !k || !q_codes || !q_scales || !k_codes || !k_scales || !k_mean) return LSD_ERR_NULL;
+  if (flags & ~(LSD_PREP_SMOOTH_K | LSD_PREP_ROTATE)) return LSD_ERR_FLAGS;
+  const bool smooth = (flags & LSD_PREP_SMOOTH_K) != 0;
+  if (!q || !k || !q_codes || !q_scales || !k_codes || !k_scales || (smooth && !k_mean)) return LSD_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_codes) || !aligned16(q_scales) ||
       !aligned16(k_codes) || !aligned16(k_scales) || !aligned16(k_mean))
     return LSD_ERR_ALIGN;
-  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lsd::prep_workspace_bytes(H, L))
+  if (smooth && (!workspace || ((uintptr_t)workspace & 255u) ||
+                 workspace_bytes < lsd::prep_workspace_bytes(H, L)))
     return LSD_ERR_WORKSPACE;
   (void)hipGetLastError();
   return launch_status(lsd::launch_qk_prep(q, k, q_codes, q_scales, k_codes, k_scales, k_mean, workspace,
-                                           H, L, (hipStream_t)stream));
+                                           H, L, smooth, (flags & LSD_PREP_ROTATE) != 0, (hipStream_t)stream));
+}
+
+int qk_prep_fp4(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8_t* q_scales,
+                uint8_t* k_codes, uint8_t* k_scales, float* k_mean, void* workspace,
+                size_t workspace_bytes, int H, int L, int d, void* stream) {
+  return qk_prep_fp4_ex(q, k, q_codes, q_scales, k_codes, k_scales, k_mean, workspace, workspace_bytes, H, L, d,
+                        LSD_PREP_SMOOTH_K | LSD_PREP_ROTATE, stream);
 }
 
 int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,

@@ -21,6 +21,6 @@ hipError_t launch_attn_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t
 size_t prep_workspace_bytes(int H, int L);
 hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uint8_t* qs,
                           uint8_t* kc, uint8_t* ks, float* kmean, void* ws, int H, int L,
-                          hipStream_t stream);
+                          bool smooth, bool rotate, hipStream_t stream);
 
 }  // namespace lsd

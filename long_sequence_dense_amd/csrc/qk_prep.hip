@@ -31,6 +31,10 @@
 //                    2^-133), combines them, rounds once to fp64 (nearest,
 //                    ties to even), divides by L in fp64 and rounds to fp32.
 //   quant (K)        as for Q after x = RN32(k - mean).
+// Ablation variants (same section: plain quantization against quantization
+// after the two transforms): without smoothing the mean kernels are skipped
+// and K is quantized as given; without the rotation the butterfly and the
+// 1/sqrt(128) factor are skipped and each block is 16 consecutive channels.
 #include "lsd_internal.h"
 #include "device_common.h"
 
@@ -90,7 +94,8 @@ __device__ __forceinline__ float dpp_xor2(float x) {
 
 // Four lanes per 128-channel row, 32 consecutive channels per lane.  grid:
 // one lane quad per row of all heads.  K (KMEAN): x = RN32(k - mean) first.
-template <bool KMEAN>
+// ROT: the rotation (otherwise y = x).
+template <bool KMEAN, bool ROT>
 __global__ __launch_bounds__(QUANT_THREADS) void quant_kernel(const uint16_t* __restrict__ src,
                                                               const float* __restrict__ kmean,
                                                               uint8_t* __restrict__ codes,
@@ -121,31 +126,33 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_kernel(const uint16_t* __
       for (int j = 0; j < 4; ++j) x[4 * i + j] = x[4 * i + j] - m4[j];
     }
   }
-  // butterfly stages 0..4: channel bits 0..4 are the register index
+  if constexpr (ROT) {
+    // butterfly stages 0..4: channel bits 0..4 are the register index
 #pragma unroll
-  for (int s = 0; s < 5; ++s) {
-    const int hs = 1 << s;
+    for (int s = 0; s < 5; ++s) {
+      const int hs = 1 << s;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if ((i & hs) == 0) {
-        const float a = x[i], b = x[i + hs];
-        x[i] = a + b;
-        x[i + hs] = a - b;
+      for (int i = 0; i < 32; ++i) {
+        if ((i & hs) == 0) {
+          const float a = x[i], b = x[i + hs];
+          x[i] = a + b;
+          x[i + hs] = a - b;
+        }
       }
     }
+    // stages 5 and 6: channel bits 5 and 6 are bits 0 and 1 of the lane in its
+    // quad.  The lane with the bit clear holds x_i and forms x_i + x_j; its
+    // partner holds x_j and forms x_i - x_j; fma(own, +-1, partner) is that one
+    // rounded operation, signed zeros included.
+    const float k5 = (part & 1) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], k5, dpp_xor1(x[i]));
+    const float k6 = (part & 2) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], k6, dpp_xor2(x[i]));
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = x[i] * kHadamardScale;
   }
-  // stages 5 and 6: channel bits 5 and 6 are bits 0 and 1 of the lane in its
-  // quad.  The lane with the bit clear holds x_i and forms x_i + x_j; its
-  // partner holds x_j and forms x_i - x_j; fma(own, +-1, partner) is that one
-  // rounded operation, signed zeros included.
-  const float k5 = (part & 1) ? -1.0f : 1.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], k5, dpp_xor1(x[i]));
-  const float k6 = (part & 2) ? -1.0f : 1.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], k6, dpp_xor2(x[i]));
-#pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = x[i] * kHadamardScale;
 
   uint32_t scode[2];
 #pragma unroll
@@ -374,6 +381,19 @@ __global__ __launch_bounds__(MEAN_THREADS) void kmean_partial_kernel(const uint1
   mean_block(k, parts, L, nparts, (int)blockIdx.y, (int)blockIdx.x);
 }
 
+__global__ void fill_zero_kernel(float* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+template <bool KMEAN, bool ROT>
+void launch_quant(const uint16_t* src, const float* kmean, uint8_t* codes, uint8_t* scales, long long nrows, int L,
+                  hipStream_t stream) {
+  const unsigned blocks = (unsigned)((nrows + (QUANT_THREADS / 4) - 1) / (QUANT_THREADS / 4));
+  hipLaunchKernelGGL((quant_kernel<KMEAN, ROT>), dim3(blocks), dim3(QUANT_THREADS), 0, stream, src, kmean, codes,
+                     scales, nrows, L);
+}
+
 }  // namespace
 
 size_t prep_workspace_bytes(int H, int L) {
@@ -381,19 +401,26 @@ size_t prep_workspace_bytes(int H, int L) {
 }
 
 hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uint8_t* qs, uint8_t* kc,
-                          uint8_t* ks, float* kmean, void* ws, int H, int L, hipStream_t stream) {
-  double* parts = (double*)ws;
-  const int nchunks = mean_chunks(L);
-  const int nparts = nchunks * MEAN_SLOTS;
+                          uint8_t* ks, float* kmean, void* ws, int H, int L, bool smooth, bool rotate,
+                          hipStream_t stream) {
   const long long nrows = (long long)H * L;
-  const unsigned qblocks = (unsigned)((nrows + (QUANT_THREADS / 4) - 1) / (QUANT_THREADS / 4));
-  hipLaunchKernelGGL(quant_kernel<false>, dim3(qblocks), dim3(QUANT_THREADS), 0, stream, q, (const float*)nullptr,
-                     qc, qs, nrows, L);
-  hipLaunchKernelGGL(kmean_partial_kernel, dim3(nchunks, H), dim3(MEAN_THREADS), 0, stream, k, parts, L, nparts);
-  hipLaunchKernelGGL(kmean_final_kernel, dim3(H * kHeadDim), dim3(FINAL_THREADS), 0, stream, k,
-                     (const double*)parts, kmean, L, nparts);
-  hipLaunchKernelGGL(quant_kernel<true>, dim3(qblocks), dim3(QUANT_THREADS), 0, stream, k, (const float*)kmean,
-                     kc, ks, nrows, L);
+  if (rotate) launch_quant<false, true>(q, nullptr, qc, qs, nrows, L, stream);
+  else launch_quant<false, false>(q, nullptr, qc, qs, nrows, L, stream);
+  if (smooth) {
+    double* parts = (double*)ws;
+    const int nchunks = mean_chunks(L);
+    const int nparts = nchunks * MEAN_SLOTS;
+    hipLaunchKernelGGL(kmean_partial_kernel, dim3(nchunks, H), dim3(MEAN_THREADS), 0, stream, k, parts, L, nparts);
+    hipLaunchKernelGGL(kmean_final_kernel, dim3(H * kHeadDim), dim3(FINAL_THREADS), 0, stream, k,
+                       (const double*)parts, kmean, L, nparts);
+    if (rotate) launch_quant<true, true>(k, kmean, kc, ks, nrows, L, stream);
+    else launch_quant<true, false>(k, kmean, kc, ks, nrows, L, stream);
+  } else {
+    if (kmean) hipLaunchKernelGGL(fill_zero_kernel, dim3((H * kHeadDim + 255) / 256), dim3(256), 0, stream, kmean,
+                                  H * kHeadDim);
+    if (rotate) launch_quant<false, true>(k, nullptr, kc, ks, nrows, L, stream);
+    else launch_quant<false, false>(k, nullptr, kc, ks, nrows, L, stream);
+  }
   return hipGetLastError();
 }
 

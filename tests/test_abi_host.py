@@ -38,8 +38,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.lsd_abi_version() == 1
-    for st in range(8):
+    assert lib.lsd_abi_version() == 2
+    for st in range(9):
         assert lib.lsd_status_str(st).decode()
     assert lib.lsd_status_str(99).decode() == "unknown status"
 
@@ -82,6 +82,19 @@ def test_prep_argument_errors(lib):
     assert f(A, A, A, A, A, A, A, N, need, 2, 16, 128, N) == 5           # null workspace
     assert f(A, A, A, A, A, A, A, ws, need - 1, 2, 16, 128, N) == 5      # too small
     assert f(A, A, A, A, A, A, A, ctypes.c_void_p(0x200010), need, 2, 16, 128, N) == 5  # not 256-aligned
+
+
+def test_prep_ex_argument_errors(lib):
+    f = lib.qk_prep_fp4_ex
+    ws = ctypes.c_void_p(0x200000)
+    need = lib.qk_prep_fp4_workspace_bytes(2, 16, 128)
+    assert f(A, A, A, A, A, A, A, ws, need, 2, 16, 128, 4, N) == 8         # unknown flag bit
+    assert f(A, A, A, A, A, A, A, ws, need, 2, 16, 128, -1, N) == 8
+    assert f(A, A, A, A, A, A, A, ws, need, 2, 16, 64, 3, N) == 3
+    assert f(A, A, A, A, A, A, N, ws, need, 2, 16, 128, 1, N) == 1         # smoothing needs k_mean
+    assert f(A, A, A, A, A, A, A, N, 0, 2, 16, 128, 3, N) == 5             # ... and the workspace
+    assert f(A, A, A, A, A, A, B, N, 0, 2, 16, 128, 2, N) == 4             # misaligned optional k_mean
+    assert f(A, A, N, A, A, A, N, N, 0, 2, 16, 128, 0, N) == 1             # null q_codes
 
 
 def test_fp4qk_argument_errors(lib):
