@@ -21,11 +21,12 @@
 //                    and the hardware E2M1 conversion with a unit
 //                    (power-of-two) scale.
 //   kmean_partial    exact partial column sums of K in fp64: a thread sums up
-//                    to 256 BF16 values per channel; all of them are multiples
-//                    of 2^(E_min-134) and below 2^(E_max-126), so the fp64 sum
-//                    is exact when E_max - E_min <= 37 (tracked per thread
-//                    with packed 16-bit min/max); otherwise the partial is
-//                    flagged and recomputed exactly by kmean_final.
+//                    to n = 256 BF16 values per channel; all of them are
+//                    multiples of 2^(E_min-134) and below 2^(E_max-126), so
+//                    the fp64 sum is exact when E_max - E_min <= 45 - log2(n)
+//                    (tracked per thread with packed 16-bit min/max);
+//                    otherwise the partial is flagged and recomputed exactly
+//                    by kmean_final.
 //   kmean_final      one wave per (head, channel): adds the exact partials
 //                    into 320-bit two's-complement integers (units of
 //                    2^-133), combines them, rounds once to fp64 (nearest,
@@ -45,6 +46,11 @@ constexpr int QUANT_THREADS = 256;              // 64 rows per iteration
 constexpr int MEAN_THREADS = QUANT_THREADS;     // 16 row slots x 16 channel groups (shares a grid)
 constexpr int MEAN_ROWS = 4096;                 // rows per column-sum workgroup
 constexpr int MEAN_SLOTS = MEAN_THREADS / 16;   // partials per channel per workgroup
+constexpr int MEAN_PER_THREAD = MEAN_ROWS / MEAN_SLOTS;   // values summed by one thread (a power of two)
+// Largest exponent span for which the fp64 sum of MEAN_PER_THREAD values is
+// certified exact: MEAN_PER_THREAD * 2^(span + 8) <= 2^53.
+constexpr int kMeanSpan = 45 - __builtin_ctz(MEAN_PER_THREAD);
+static_assert((MEAN_PER_THREAD & (MEAN_PER_THREAD - 1)) == 0, "rows per thread must be a power of two");
 constexpr float kHadamardScale = 0x1.6a09e6p-4f;   // RN32(1/sqrt(128)), bits 0x3DB504F3
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -93,35 +99,50 @@ __device__ __forceinline__ float dpp_xor2(float x) {
 }
 
 // Four lanes per 128-channel row, 32 consecutive channels per lane.  grid:
-// one lane quad per row of all heads.  K (KMEAN): x = RN32(k - mean) first.
-// ROT: the rotation (otherwise y = x).
+// (row blocks of one head, heads), one lane quad per row.  K (KMEAN):
+// x = RN32(k - mean) first.  ROT: the rotation (otherwise y = x).
 template <bool KMEAN, bool ROT>
 __global__ __launch_bounds__(QUANT_THREADS) void quant_kernel(const uint16_t* __restrict__ src,
                                                               const float* __restrict__ kmean,
                                                               uint8_t* __restrict__ codes,
-                                                              uint8_t* __restrict__ scales, long long nrows,
-                                                              int L) {
+                                                              uint8_t* __restrict__ scales, int L) {
   const int tid = threadIdx.x;
   const int part = tid & 3;                      // channels 32*part .. 32*part+31
-  const long long row = (long long)blockIdx.x * (QUANT_THREADS / 4) + (tid >> 2);
-  if (row >= nrows) return;                      // whole lane quads leave together
-
+  const int r = blockIdx.x * (QUANT_THREADS / 4) + (tid >> 2);
+  const int h = blockIdx.y;
+  const bool valid = r < L;
+  if constexpr (!KMEAN) {
+    if (!valid) return;                          // whole lane quads leave together
+  }
+  const long long row = (long long)h * L + r;
   const uint16_t* rp = src + row * kHeadDim + part * 32;
+  u32x4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = (!KMEAN || valid) ? *(const u32x4*)(rp + 8 * i) : (u32x4)0;
+  // Every row of the workgroup is in head h: its mean is read once into LDS,
+  // by the first 32 threads, before any thread leaves.
+  __shared__ __attribute__((aligned(16))) float km[kHeadDim];
+  if constexpr (KMEAN) {
+    if (tid < kHeadDim / 4) *(f32x4*)(km + 4 * tid) = *(const f32x4*)(kmean + h * kHeadDim + 4 * tid);
+    __syncthreads();
+  }
+  if constexpr (KMEAN) {
+    if (!valid) return;
+  }
+
   float x[32];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4 raw = *(const u32x4*)(rp + 8 * i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[8 * i + 2 * j] = __uint_as_float(raw[j] << 16);
-      x[8 * i + 2 * j + 1] = __uint_as_float(raw[j] & 0xFFFF0000u);
+      x[8 * i + 2 * j] = __uint_as_float(raw[i][j] << 16);
+      x[8 * i + 2 * j + 1] = __uint_as_float(raw[i][j] & 0xFFFF0000u);
     }
   }
   if constexpr (KMEAN) {
-    const float* km = kmean + (row / L) * kHeadDim + part * 32;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const f32x4 m4 = *(const f32x4*)(km + 4 * i);
+      const f32x4 m4 = *(const f32x4*)(km + part * 32 + 4 * i);
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[4 * i + j] = x[4 * i + j] - m4[j];
     }
@@ -195,8 +216,8 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_kernel(const uint16_t* __
 
 // ---------------------------------------------------------------- mean -------
 
-// Exact partial column sums of rows chunk*4096 .. +4095 of head h.  Thread t:
-// channels 8*(t%16) .. +7, rows r0 + t/16 + 16*i.
+// Exact partial column sums of rows chunk*MEAN_ROWS .. +MEAN_ROWS-1 of head h.
+// Thread t: channels 8*(t%16) .. +7, rows r0 + t/16 + 16*i.
 __device__ __forceinline__ void mean_block(const uint16_t* __restrict__ k, double* __restrict__ parts, int L,
                                            int nparts, int h, int chunk) {
   const int tid = threadIdx.x;
@@ -209,13 +230,14 @@ __device__ __forceinline__ void mean_block(const uint16_t* __restrict__ k, doubl
   for (int j = 0; j < 8; ++j) acc[j] = 0.0;
   u16x2 emax = {0, 0};                          // max magnitude bits (sign cleared)
   u16x2 emin = {0xFFFF, 0xFFFF};                // min of (magnitude bits - 1): zero never wins
-  for (int r = r0 + slot; r < r1; r += 4 * MEAN_SLOTS) {
-    u32x4 w[4];                                  // four rows in flight; rows past the end add zero
+  constexpr int U = 4;                           // rows in flight per thread
+  for (int r = r0 + slot; r < r1; r += U * MEAN_SLOTS) {
+    u32x4 w[U];                                  // rows past the end add zero
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
       w[u] = r + u * MEAN_SLOTS < r1 ? *(const u32x4*)(base + (size_t)(r + u * MEAN_SLOTS) * kHeadDim) : (u32x4)0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         acc[2 * j] += (double)__uint_as_float(w[u][j] << 16);
@@ -233,7 +255,7 @@ __device__ __forceinline__ void mean_block(const uint16_t* __restrict__ k, doubl
     const int e_max = (int)(mx >> 7);
     int e_min = (int)((mn + 1) >> 7);
     e_min = e_min < 1 ? 1 : e_min;               // subnormals share exponent 1's quantum
-    exact = e_max - e_min <= 37;                 // at most 256 values per partial
+    exact = e_max - e_min <= kMeanSpan;
   }
   double* out = parts + ((size_t)h * kHeadDim + 8 * g) * nparts + (size_t)chunk * MEAN_SLOTS + slot;
 #pragma unroll
@@ -387,11 +409,11 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int n) {
 }
 
 template <bool KMEAN, bool ROT>
-void launch_quant(const uint16_t* src, const float* kmean, uint8_t* codes, uint8_t* scales, long long nrows, int L,
+void launch_quant(const uint16_t* src, const float* kmean, uint8_t* codes, uint8_t* scales, int H, int L,
                   hipStream_t stream) {
-  const unsigned blocks = (unsigned)((nrows + (QUANT_THREADS / 4) - 1) / (QUANT_THREADS / 4));
-  hipLaunchKernelGGL((quant_kernel<KMEAN, ROT>), dim3(blocks), dim3(QUANT_THREADS), 0, stream, src, kmean, codes,
-                     scales, nrows, L);
+  const unsigned blocks = (unsigned)((L + (QUANT_THREADS / 4) - 1) / (QUANT_THREADS / 4));
+  hipLaunchKernelGGL((quant_kernel<KMEAN, ROT>), dim3(blocks, H), dim3(QUANT_THREADS), 0, stream, src, kmean, codes,
+                     scales, L);
 }
 
 }  // namespace
@@ -403,9 +425,8 @@ size_t prep_workspace_bytes(int H, int L) {
 hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uint8_t* qs, uint8_t* kc,
                           uint8_t* ks, float* kmean, void* ws, int H, int L, bool smooth, bool rotate,
                           hipStream_t stream) {
-  const long long nrows = (long long)H * L;
-  if (rotate) launch_quant<false, true>(q, nullptr, qc, qs, nrows, L, stream);
-  else launch_quant<false, false>(q, nullptr, qc, qs, nrows, L, stream);
+  if (rotate) launch_quant<false, true>(q, nullptr, qc, qs, H, L, stream);
+  else launch_quant<false, false>(q, nullptr, qc, qs, H, L, stream);
   if (smooth) {
     double* parts = (double*)ws;
     const int nchunks = mean_chunks(L);
@@ -413,13 +434,13 @@ hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uin
     hipLaunchKernelGGL(kmean_partial_kernel, dim3(nchunks, H), dim3(MEAN_THREADS), 0, stream, k, parts, L, nparts);
     hipLaunchKernelGGL(kmean_final_kernel, dim3(H * kHeadDim), dim3(FINAL_THREADS), 0, stream, k,
                        (const double*)parts, kmean, L, nparts);
-    if (rotate) launch_quant<true, true>(k, kmean, kc, ks, nrows, L, stream);
-    else launch_quant<true, false>(k, kmean, kc, ks, nrows, L, stream);
+    if (rotate) launch_quant<true, true>(k, kmean, kc, ks, H, L, stream);
+    else launch_quant<true, false>(k, kmean, kc, ks, H, L, stream);
   } else {
     if (kmean) hipLaunchKernelGGL(fill_zero_kernel, dim3((H * kHeadDim + 255) / 256), dim3(256), 0, stream, kmean,
                                   H * kHeadDim);
-    if (rotate) launch_quant<false, true>(k, nullptr, kc, ks, nrows, L, stream);
-    else launch_quant<false, false>(k, nullptr, kc, ks, nrows, L, stream);
+    if (rotate) launch_quant<false, true>(k, nullptr, kc, ks, H, L, stream);
+    else launch_quant<false, false>(k, nullptr, kc, ks, H, L, stream);
   }
   return hipGetLastError();
 }

@@ -47,6 +47,8 @@ def test_version_and_status_strings(lib):
 def test_workspace_query(lib):
     # exact fp64 partial sums: 16 per 4096-row chunk per (head, channel)
     assert lib.qk_prep_fp4_workspace_bytes(40, 109000, 128) == 40 * 128 * 27 * 16 * 8
+    assert lib.qk_prep_fp4_workspace_bytes(2, 4096, 128) == 2 * 128 * 1 * 16 * 8
+    assert lib.qk_prep_fp4_workspace_bytes(2, 4097, 128) == 2 * 128 * 2 * 16 * 8
     assert lib.qk_prep_fp4_workspace_bytes(1, 1, 128) == 128 * 16 * 8
     assert lib.qk_prep_fp4_workspace_bytes(0, 10, 128) == 0
     assert lib.qk_prep_fp4_workspace_bytes(1, 10, 64) == 0
