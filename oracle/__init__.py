@@ -14,6 +14,7 @@ Contents
                       variants (no smoothing, no rotation).
 ``oracle.fp4_error``  relative attention error of the FP4-QK variants against
                       exact attention.
+``oracle.attention_bwd`` fp64 gradients of attention (dQ, dK, dV).
 
 Source: "Pika H3 Flex in FastVideo: 7x Faster, and Near Real Time in 4-bit"
 (haoailab blog), sections "Faster at BF16" and "FP4 attention".  Every function
@@ -36,3 +37,4 @@ from .nvfp4 import (  # noqa: F401
     dequant_nvfp4,
 )
 from .fp4_error import fp4_attention_error, fp4_outputs, relative_error  # noqa: F401
+from .attention_bwd import attention_bwd_fp64, attention_bwd_dq_rows_fp64  # noqa: F401

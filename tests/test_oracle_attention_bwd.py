@@ -1,0 +1,117 @@
+"""Pins for the fp64 attention-gradient oracle (CPU only).
+
+The gradients are checked against central finite differences of the forward
+oracle's <dO, O> (itself pinned by brute force), against closed forms and
+exact sums that follow from softmax rows summing to one, and against the
+covariance of dQ, dK under a shared orthonormal rotation of Q and K (the
+rotation of "Pika H3 Flex in FastVideo: 7x Faster, and Near Real Time in
+4-bit", section "FP4 attention").  Planted mistakes in a copy of the gradient
+formulas fail the finite differences.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle.attention import attention_fp64
+from oracle.attention_bwd import attention_bwd_dq_rows_fp64, attention_bwd_fp64
+
+
+def loss(q, k, v, do, scale):
+    o, _ = attention_fp64(q, k, v, scale)
+    return float((o * do).sum())
+
+
+def finite_diff(q, k, v, do, scale, which, h=1e-6):
+    args = {"q": q, "k": k, "v": v}
+    x = args[which]
+    g = np.zeros_like(x)
+    for idx in np.ndindex(*x.shape):
+        xp = x.copy()
+        xm = x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        ap = dict(args, **{which: xp})
+        am = dict(args, **{which: xm})
+        g[idx] = (loss(ap["q"], ap["k"], ap["v"], do, scale) - loss(am["q"], am["k"], am["v"], do, scale)) / (2 * h)
+    return g
+
+
+def tiny(seed, H=1, L=5, d=8):
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal((H, L, d)) for _ in range(4)]
+
+
+@pytest.mark.parametrize("seed,L,d", [(0, 5, 8), (1, 3, 16), (2, 7, 4)])
+def test_gradients_match_finite_differences(seed, L, d):
+    q, k, v, do = tiny(seed, 1, L, d)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, scale)
+    for name, g in (("q", dq), ("k", dk), ("v", dv)):
+        fd = finite_diff(q, k, v, do, scale, name)
+        assert np.max(np.abs(g - fd)) <= 1e-7 * (1 + np.max(np.abs(fd))), name
+
+
+def test_single_key_closed_form():
+    q, k, v, do = tiny(3, 2, 1, 16)
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, 0.3)
+    assert np.array_equal(dv, do)
+    assert np.all(dq == 0) and np.all(dk == 0)
+
+
+def test_identical_keys_give_zero_dq():
+    q, k, v, do = tiny(4, 1, 6, 8)
+    k[:] = k[:, :1]
+    dq, _, _ = attention_bwd_fp64(q, k, v, do, 0.5)
+    assert np.max(np.abs(dq)) <= 1e-15
+
+
+def test_softmax_sums():
+    # every softmax row sums to one: sum_j dS_ij = 0, so the key-side gradient
+    # dK sums to zero over keys, and dV sums over keys to the sum of dO.
+    rng = np.random.default_rng(5)
+    q, k, v, do = (rng.standard_normal((2, 300, 32)) for _ in range(4))
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, 0.2, block=77)
+    assert np.max(np.abs(dk.sum(axis=1))) <= 1e-11 * np.max(np.abs(dk)) * 300
+    assert np.max(np.abs(dv.sum(axis=1) - do.sum(axis=1))) <= 1e-11 * 300
+
+
+def test_rotation_covariance():
+    rng = np.random.default_rng(6)
+    q, k, v, do = (rng.standard_normal((1, 40, 16)) for _ in range(4))
+    hm, _ = np.linalg.qr(rng.standard_normal((16, 16)))
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, 0.25)
+    dq2, dk2, dv2 = attention_bwd_fp64(q @ hm, k @ hm, v, do, 0.25)
+    assert np.max(np.abs(dq2 - dq @ hm)) <= 1e-12
+    assert np.max(np.abs(dk2 - dk @ hm)) <= 1e-12
+    assert np.max(np.abs(dv2 - dv)) <= 1e-12
+
+
+def test_blocking_and_rows_agree():
+    rng = np.random.default_rng(7)
+    q, k, v, do = (rng.standard_normal((2, 130, 16)) for _ in range(4))
+    a = attention_bwd_fp64(q, k, v, do, 0.3)
+    b = attention_bwd_fp64(q, k, v, do, 0.3, block=17)
+    for x, y in zip(a, b):
+        assert np.max(np.abs(x - y)) <= 1e-12
+    rows = np.array([0, 64, 129])
+    dqr = attention_bwd_dq_rows_fp64(q[1, rows], k[1], v[1], do[1, rows], 0.3)
+    assert np.max(np.abs(dqr - a[0][1, rows])) <= 1e-12
+
+
+def test_planted_mistakes_fail():
+    q, k, v, do = tiny(8, 1, 5, 8)
+    scale = 1.0 / math.sqrt(8)
+    fdq = finite_diff(q, k, v, do, scale, "q")
+    fdk = finite_diff(q, k, v, do, scale, "k")
+    s = scale * q[0] @ k[0].T
+    p = np.exp(s - s.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    dp = do[0] @ v[0].T
+    good = p * (dp - (p * dp).sum(1, keepdims=True))
+    no_d = p * dp                                          # D term dropped
+    wrong = [scale * no_d @ k[0], good @ k[0], scale * good.T @ k[0]]   # no D; no scale; dS transposed
+    for w in wrong:
+        assert np.max(np.abs(w - fdq[0])) > 1e-3
+    assert np.max(np.abs(scale * good @ q[0] - fdk[0])) > 1e-3   # dS instead of dS^T for dK
