@@ -1,14 +1,16 @@
 /*
  * lsd_attn.h - dense long-sequence attention on AMD MI355X (gfx950).
  *
- * C ABI of liblsd_attn.so.  Three operations over per-head token tensors
- * laid out [H, L, d] (row-major: head, token, channel), d = 128:
+ * C ABI of liblsd_attn.so.  Operations over per-head token tensors laid
+ * out [H, L, d] (row-major: head, token, channel), d = 128:
  *
  *   attn_fwd_bf16   dense non-causal softmax attention, BF16 in and out.
  *   qk_prep_fp4     mean-key subtraction, shared 128-point Hadamard rotation
- *                   and NVFP4 block quantization of Q and K.
+ *                   and NVFP4 block quantization of Q and K (qk_prep_fp4_ex:
+ *                   the same with either transform switched off).
  *   attn_fwd_fp4qk  attention whose scores come from the NVFP4 Q and K;
  *                   probabilities and V stay BF16.
+ *   attn_bwd_bf16   gradients of attn_fwd_bf16 with respect to Q, K and V.
  *
  * The method is the one of "Pika H3 Flex in FastVideo: 7x Faster, and Near
  * Real Time in 4-bit" (haoailab blog): section "Faster at BF16" (dense
@@ -160,6 +162,36 @@ int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales,
                    const uint8_t* k_codes, const uint8_t* k_scales,
                    const uint16_t* v, uint16_t* o, float* lse,
                    int H, int L, int d, float softmax_scale, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd_bf16 needs (0 on a bad shape):
+ * 2 * H * L * 4 (one fp32 row statistic pair per query row).
+ */
+size_t attn_bwd_bf16_workspace_bytes(int H, int L, int d);
+
+/*
+ * attn_bwd_bf16 - gradients of attn_fwd_bf16 with respect to Q, K and V.
+ *   q, k, v : [H, L, d] BF16 bits, the forward's inputs.
+ *   o       : [H, L, d] BF16 bits, the forward's output.
+ *   lse     : [H, L] float32, the forward's natural-log LSE (required).
+ *   dout    : [H, L, d] BF16 bits, the gradient of the loss with respect to o.
+ *   dq, dk, dv : [H, L, d] BF16 bits, written (round to nearest even of the
+ *             fp32 results).  Must not alias any input.
+ *   workspace : device buffer of at least attn_bwd_bf16_workspace_bytes
+ *             bytes, 256-byte aligned; contents unspecified on return.
+ *   softmax_scale : the sigma of the forward.
+ * With P = exp(sigma Q K^T - LSE): dV = P^T dO, dP = dO V^T,
+ * D = rowsum(dO * O), dS = P * (dP - D), dQ = sigma dS K, dK = sigma dS^T Q.
+ * P and dS are rounded to BF16 for the matrix-core products; sums are fp32.
+ * Deterministic (no atomics).  Same shape limits as attn_fwd_bf16.
+ * Source: "NVFP4 QAD" and "FP4 attention" (the model is trained with the
+ * deployed attention in the loop); the gradients are those of the forward.
+ */
+int attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const uint16_t* o, const float* lse, const uint16_t* dout,
+                  uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                  void* workspace, size_t workspace_bytes,
+                  int H, int L, int d, float softmax_scale, void* stream);
 
 #ifdef __cplusplus
 }

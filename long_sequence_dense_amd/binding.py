@@ -36,6 +36,8 @@ SIGNATURES = {
     "qk_prep_fp4": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _P]),
     "qk_prep_fp4_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _P]),
     "attn_fwd_fp4qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
+    "attn_bwd_bf16_workspace_bytes": (_S, [_I, _I, _I]),
+    "attn_bwd_bf16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _F, _P]),
 }
 
 _lib = None
@@ -205,3 +207,31 @@ def attn_fwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o=None, lse=None,
                                        _ptr(v), _ptr(o), _ptr(lse), H, L, d, scale, _stream(stream))
     _check("attn_fwd_fp4qk", st)
     return o
+
+
+def attn_bwd_bf16_workspace_bytes(H, L, d=HEAD_DIM):
+    return int(load_library().attn_bwd_bf16_workspace_bytes(H, L, d))
+
+
+def attn_bwd_bf16(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, softmax_scale=None,
+                  workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of attn_fwd_bf16; o and lse are its outputs."""
+    import torch
+    H, L, d = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, n, _bf16_types(), (H, L, d))
+    _need(lse, "lse", (torch.float32,), (H, L))
+    outs = []
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty((H, L, d), dtype=torch.bfloat16, device=q.device)
+        _need(t, n, _bf16_types(), (H, L, d))
+        outs.append(t)
+    if workspace is None:
+        workspace = torch.empty(attn_bwd_bf16_workspace_bytes(H, L, d), dtype=torch.uint8, device=q.device)
+    scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    st = load_library().attn_bwd_bf16(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), H, L, d, scale, _stream(stream))
+    _check("attn_bwd_bf16", st)
+    return tuple(outs)

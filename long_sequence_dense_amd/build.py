@@ -25,6 +25,7 @@ COMMON = [
 SOURCES = {
     "abi.hip": [],
     "attn_fwd.hip": ["-fno-honor-nans"],
+    "attn_bwd.hip": ["-fno-honor-nans"],
     "qk_prep.hip": ["-ffp-contract=off"],
 }
 

@@ -111,4 +111,27 @@ int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
                                               softmax_scale * kLog2e, (hipStream_t)stream));
 }
 
+size_t attn_bwd_bf16_workspace_bytes(int H, int L, int d) {
+  if (check_shape(H, L, d) != LSD_OK) return 0;
+  return lsd::attn_bwd_workspace_bytes(H, L);
+}
+
+int attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o, const float* lse,
+                  const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
+                  size_t workspace_bytes, int H, int L, int d, float softmax_scale, void* stream) {
+  int st = check_shape(H, L, d);
+  if (st != LSD_OK) return st;
+  if ((st = check_attn_len(L)) != LSD_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return LSD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
+    return LSD_ERR_ALIGN;
+  if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lsd::attn_bwd_workspace_bytes(H, L))
+    return LSD_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, H, L, softmax_scale,
+                                            (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -17,6 +17,12 @@ hipError_t launch_attn_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t
                              const uint8_t* ks, const uint16_t* v, uint16_t* o, float* lse,
                              int H, int L, float scale_log2, hipStream_t stream);
 
+// attention backward (attn_bwd.hip)
+size_t attn_bwd_workspace_bytes(int H, int L);
+hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                           const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                           void* ws, int H, int L, float scale, hipStream_t stream);
+
 // Q/K preparation (qk_prep.hip)
 size_t prep_workspace_bytes(int H, int L);
 hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uint8_t* qs,

@@ -13,7 +13,8 @@ shared key bias and the scaled-up outlier channels.  Head count and head size
 
 Recipe, per tensor and head (every head regenerates independently):
   rng = numpy Generator(PCG64(SeedSequence([seed, tensor_id, head])))
-  tensor_id: Q = 0, K = 1, V = 2, key offset = 3, outlier channels = 4
+  tensor_id: Q = 0, K = 1, V = 2, key offset = 3, outlier channels = 4,
+             upstream gradient dO (for the backward) = 5
   normal draws: rng.standard_normal((L, d), float32)
   Student-t draws: rng.standard_t(3, (L, d)) in float64, cast to float32
   scaling (1/sqrt(d) on Q, x20 on outlier channels) is a float32 multiply;
@@ -31,7 +32,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 D = 128
-TID_Q, TID_K, TID_V, TID_OFFSET, TID_OUTLIER = 0, 1, 2, 3, 4
+TID_Q, TID_K, TID_V, TID_OFFSET, TID_OUTLIER, TID_DOUT = 0, 1, 2, 3, 4, 5
 N_OUTLIER_CHANNELS = 3          # round(0.02 * 128)
 OUTLIER_GAIN = np.float32(20.0)
 
@@ -112,9 +113,9 @@ def _draw(dist, rng, L):
 
 
 def head_tensor(cfg, which, head):
-    """One head of Q, K or V as BF16 bits [L, d]."""
-    tid = {"q": TID_Q, "k": TID_K, "v": TID_V}[which]
-    dist = {"q": cfg.q_dist, "k": cfg.k_dist, "v": cfg.v_dist}[which]
+    """One head of Q, K, V or dO (N(0,1)) as BF16 bits [L, d]."""
+    tid = {"q": TID_Q, "k": TID_K, "v": TID_V, "do": TID_DOUT}[which]
+    dist = {"q": cfg.q_dist, "k": cfg.k_dist, "v": cfg.v_dist, "do": "normal"}[which]
     x = _draw(dist, _rng(cfg.seed, tid, head), cfg.L)
     if which == "q" and cfg.q_prescale:
         x *= np.float32(INV_SQRT_D)
@@ -136,7 +137,7 @@ def _threads():
 
 
 def make_tensor(cfg, which, heads=None, out=None):
-    """BF16 bits [len(heads), L, d] for tensor ``which`` in {q, k, v}."""
+    """BF16 bits [len(heads), L, d] for tensor ``which`` in {q, k, v, do}."""
     hs = list(range(cfg.H)) if heads is None else list(heads)
     if out is None:
         out = np.empty((len(hs), cfg.L, D), dtype=np.uint16)
