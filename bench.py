@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "bf16"], default="all",
                     help="bf16: time only attn_fwd_bf16 (for profiling runs)")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the extra (not in value) timing of attn_bwd_bf16")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for hardware-counter runs: one %d-byte torch copy (counter calibration), "
                          "then one launch of each kernel on the benchmark workload; no timing" % COPY_PROBE_BYTES)
@@ -237,6 +239,36 @@ def main():
         paths["attn_fwd_fp4qk"] = {"ms": round(t_fp4, 3), "TFLOP/s": round(a4, 1),
                                    "frac_of_peak": round(a4 / PEAK_BF16_TFLOPS, 4),
                                    "mfma_precision": "bf16 (exact dequantization of NVFP4 Q/K)"}
+    if args.only != "bf16" and not args.no_bwd:
+        # Extra path, outside the step and its value: the backward of the BF16
+        # path on the same inputs, dO ~ N(0, 1); 1 warm-up + 3 timed calls.
+        log("timing attn_bwd_bf16 (3 calls) ...")
+        lse = torch.empty((H, L), dtype=torch.float32, device=dev)
+        binding.attn_fwd_bf16(x4["q"], x4["k"], x4["v"], o4, lse, cfg4.scale, stream)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5)
+        dout = torch.randn((H, L, d), dtype=torch.float32, device=dev, generator=gen).to(torch.bfloat16)
+        grads = [torch.empty((H, L, d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+        bws = torch.empty(binding.attn_bwd_bf16_workspace_bytes(H, L, d), dtype=torch.uint8, device=dev)
+        times = []
+        for i in range(4):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            binding.attn_bwd_bf16(x4["q"], x4["k"], x4["v"], o4, lse, dout, *grads, softmax_scale=cfg4.scale,
+                                  workspace=bws, stream=stream)
+            b.record(stream)
+            b.synchronize()
+            if i:
+                times.append(a.elapsed_time(b))
+        t_bwd = sum(times) / len(times)
+        bw = 2.5 * fl / (t_bwd * 1e-3) / 1e12
+        paths["attn_bwd_bf16"] = {"ms": round(t_bwd, 3), "TFLOP/s": round(bw, 1),
+                                  "frac_of_peak": round(bw / PEAK_BF16_TFLOPS, 4),
+                                  "flop_convention": "2.5 x forward (5 of the 2HL^2d products); the kernels "
+                                                     "compute 7 (S and dP again for dQ)",
+                                  "in_value": False}
+        del grads, dout, bws
     traffic = stored_traffic()
     res = {
         "metric": METRIC,

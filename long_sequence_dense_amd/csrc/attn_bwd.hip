@@ -11,10 +11,12 @@
 // Three launches, deterministic (no atomics):
 //   bwd_rowdot  D_i = dO_i . O_i in fp32 (BF16 products are exact in fp32)
 //               and LSE_i * log2(e), into the workspace.
-//   bwd_dkdv    one wave per 32 keys (four waves, one per SIMD, per
-//               workgroup of 128 keys): K and V of its keys stay in
-//               registers as MFMA B operands; 32-query tiles of Q and dO
-//               stream through LDS (double-buffered).  Per tile: S and dP on
+//   bwd_dkdv    one wave per 32 keys (eight waves, two per SIMD, per
+//               workgroup of 256 keys): K of its keys stays in registers and
+//               the workgroup's V rows in LDS, both read as MFMA B operands;
+//               32-query tiles of Q, dO and their row statistics stream
+//               through LDS (double-buffered, copied by LDS-DMA loads so that
+//               no registers hold the next tile).  Per tile: S and dP on
 //               the 32x32x16 BF16 MFMA with the query tile as the A operand
 //               (rows = queries, columns = this wave's keys), P and dS on the
 //               VALU, then dV^T += dO^T P and dK^T += Q^T dS with the
@@ -28,8 +30,8 @@
 //               tiles of K and V through LDS.  S^T = K Q^T, dP^T = V dO^T,
 //               dS^T on the VALU, dQ^T += K^T dS^T.
 // P and dS are rounded to BF16 for their MFMAs; all sums are fp32.  Rows past
-// L are zero-filled by the buffer loads (their keys then add nothing) and get
-// an infinite LSE (their probabilities are zero).
+// L are zero-filled by the buffer loads: their keys add nothing, and their
+// queries meet only zero operands (bwd_dq gives them an infinite LSE).
 #include "lsd_internal.h"
 #include "device_common.h"
 
@@ -50,6 +52,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t 
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+// Memory -> LDS without registers: buffer_load_dword with the LDS flag writes
+// lane j's dword to M0 + 4 j (one 256-byte row per wave instruction).  Byte
+// offsets go in the per-lane offset so the range check sees them: rows past
+// the end are written as zeros.  Inline assembly so that the compiler does
+// not wait for these loads before reading the other LDS buffer; the caller
+// waits (vmcnt 0) before the barrier that publishes the data.  M0 is written
+// by SALU and read by the load one instruction later (s_nop: the M0 read
+// hazard of LDS DMA).
+struct Rsrc {
+  u32x4 w;
+};
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  Rsrc r;
+  r.w[0] = (uint32_t)a;
+  r.w[1] = (uint32_t)(a >> 32) & 0xFFFFu;     // stride 0
+  r.w[2] = bytes;
+  r.w[3] = 0x00020000u;
+  return r;
+}
+__device__ __forceinline__ void dma_dword(const Rsrc& r, const void* lds_dst, int voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r.w)
+               : "m0");
+}
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 // A operand from rows of a row-major LDS tile: lane l reads row l % 32,
 // channels 16 * kk + 8 * (l / 32) .. +7.  `lane_row` = (l % 32) * TS + 8 * (l / 32).
@@ -155,7 +186,7 @@ __global__ __launch_bounds__(ROWDOT_THREADS) void bwd_rowdot_kernel(const uint16
 
 // ------------------------------------------------------------------- dK dV --
 
-constexpr int DKDV_WAVES = 4;
+constexpr int DKDV_WAVES = 8;
 constexpr int DKDV_THREADS = 64 * DKDV_WAVES;
 constexpr int DKDV_KEYS = 32 * DKDV_WAVES;     // keys per workgroup
 
@@ -174,11 +205,13 @@ struct DkdvParams {
   float scale;                                  // softmax scale
 };
 
+constexpr int VKS = kHeadDim + 8;       // row stride (bf16) of the stationary V rows: 272 B
 struct DkdvSmem {
   uint16_t q[2][TILE];
   uint16_t dout[2][TILE];
   float lse2[2][TR];
   float dsum[2][TR];
+  uint16_t v[DKDV_KEYS * VKS];          // the workgroup's V rows, read as B operands
 };
 
 __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p) {
@@ -193,24 +226,33 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
   const int L = p.L;
   const size_t head_row0 = (size_t)h * (size_t)L;
   const size_t head_bytes = (size_t)L * kHeadDim * 2;
-  const __amdgpu_buffer_rsrc_t rq = rsrc(p.q + head_row0 * kHeadDim, head_bytes);
-  const __amdgpu_buffer_rsrc_t rdo = rsrc(p.dout + head_row0 * kHeadDim, head_bytes);
-  const float* lse2_h = p.lse2 + head_row0;
-  const float* dsum_h = p.dsum + head_row0;
+  const Rsrc rq = make_rsrc(p.q + head_row0 * kHeadDim, (uint32_t)head_bytes);
+  const Rsrc rdo = make_rsrc(p.dout + head_row0 * kHeadDim, (uint32_t)head_bytes);
+  const Rsrc rl = make_rsrc(p.lse2 + head_row0, (uint32_t)L * 4);
+  const Rsrc rd = make_rsrc(p.dsum + head_row0, (uint32_t)L * 4);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // This wave's 32 keys: K and V rows as B operands (8 chunks of 16 channels).
   const int key = kt * DKDV_KEYS + wave * 32 + ln.l32;
   const bool kvalid = key < L;
-  bf16x8 kreg[8], vreg[8];
+  bf16x8 kreg[8];
   {
     const uint16_t* kp = p.k + (head_row0 + (size_t)(kvalid ? key : 0)) * kHeadDim + 8 * ln.hf;
-    const uint16_t* vp = p.v + (head_row0 + (size_t)(kvalid ? key : 0)) * kHeadDim + 8 * ln.hf;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < 8; ++kk)
       kreg[kk] = __builtin_bit_cast(bf16x8, kvalid ? *(const u16x8*)(kp + 16 * kk) : (u16x8)0);
-      vreg[kk] = __builtin_bit_cast(bf16x8, kvalid ? *(const u16x8*)(vp + 16 * kk) : (u16x8)0);
+    // V rows of the workgroup's keys into LDS (zeros past L): 256 rows of 16
+    // chunks, 8 per thread.
+    const __amdgpu_buffer_rsrc_t rv = rsrc(p.v + head_row0 * kHeadDim, head_bytes);
+    const int key0 = kt * DKDV_KEYS;
+#pragma unroll
+    for (int i = 0; i < DKDV_KEYS * 16 / DKDV_THREADS; ++i) {
+      const int id = tid + DKDV_THREADS * i;
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rv, key0 * (kHeadDim * 2) + id * 16, 0, 0);
+      *(u32x4*)(sm.v + (id >> 4) * VKS + (id & 15) * 8) = x;
     }
   }
+  const int v_lane = (wave * 32 + ln.l32) * VKS + 8 * ln.hf;      // this lane's V row, channel half
   f32x16 dvacc[4], dkacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
@@ -218,34 +260,32 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
     dkacc[db] = (f32x16)0.0f;
   }
 
-  // Row statistics of a query tile: rows past L get LSE = +inf (P = 0), D = 0.
-  auto load_stats = [&](int q0, int buf) {
-    if (tid < TR) {
-      const int r = q0 + tid;
-      sm.lse2[buf][tid] = r < L ? lse2_h[r] : __builtin_inff();
-      sm.dsum[buf][tid] = r < L ? dsum_h[r] : 0.0f;
+  // Query tile q0 into LDS buffer buf: each wave copies 4 rows of Q and of
+  // dO (one row per instruction), waves 0 and 1 the 32 LSE2 and D values.
+  // Rows past L arrive as zeros: their Q and dO rows are zero, so their
+  // probabilities (exp2(0 - 0) = 1) meet only zero operands below and their
+  // dS is zero.
+  auto stage = [&](int q0, int buf) {
+#pragma unroll
+    for (int i = 0; i < TR / DKDV_WAVES; ++i) {
+      const int r = wave_u * (TR / DKDV_WAVES) + i;
+      const int voff = (q0 + r) * (kHeadDim * 2) + 4 * ln.lane;
+      dma_dword(rq, sm.q[buf] + r * TS, voff);
+      dma_dword(rdo, sm.dout[buf] + r * TS, voff);
     }
+    if (wave_u == 0 && ln.lane < TR) dma_dword(rl, sm.lse2[buf], 4 * (q0 + ln.lane));
+    if (wave_u == 1 && ln.lane < TR) dma_dword(rd, sm.dsum[buf], 4 * (q0 + ln.lane));
   };
 
   const int ntiles = (L + TR - 1) / TR;
-  {
-    RowStage<DKDV_THREADS> sq, sd;
-    load_rows(rq, 0, tid, sq);
-    load_rows(rdo, 0, tid, sd);
-    load_stats(0, 0);
-    store_rows(sm.q[0], tid, sq);
-    store_rows(sm.dout[0], tid, sd);
-  }
+  stage(0, 0);
+  dma_wait();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    RowStage<DKDV_THREADS> sq, sd;
     const bool more = t + 1 < ntiles;
-    if (more) {
-      load_rows(rq, (t + 1) * TR, tid, sq);
-      load_rows(rdo, (t + 1) * TR, tid, sd);
-    }
+    if (more) stage((t + 1) * TR, buf ^ 1);
     const uint16_t* qt = sm.q[buf];
     const uint16_t* dt = sm.dout[buf];
     // S = Q K^T and dP = dO V^T for this wave's keys: rows = queries.
@@ -253,7 +293,9 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) s = mfma(row_operand(qt, ln.lane_row, kk), kreg[kk], s);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) dp = mfma(row_operand(dt, ln.lane_row, kk), vreg[kk], dp);
+    for (int kk = 0; kk < 8; ++kk)
+      dp = mfma(row_operand(dt, ln.lane_row, kk), __builtin_bit_cast(bf16x8, *(const u16x8*)(sm.v + v_lane + 16 * kk)),
+                dp);
     // P = exp2(S c - LSE2) and dS = P (dP - D); accumulator element i is
     // query row 8 * (i / 4) + 4 * hf + i % 4 of the tile.
     f32x8 pf[2], df[2];
@@ -285,11 +327,7 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
 #pragma unroll
       for (int db = 0; db < 4; ++db) dkacc[db] = mfma(tr_operand(qt, ln.lane_tr, cc, db), dsb[cc], dkacc[db]);
 
-    if (more) {
-      load_stats((t + 1) * TR, buf ^ 1);
-      store_rows(sm.q[buf ^ 1], tid, sq);
-      store_rows(sm.dout[buf ^ 1], tid, sd);
-    }
+    dma_wait();
     __syncthreads();
   }
 
