@@ -11,6 +11,8 @@
  *   attn_fwd_fp4qk  attention whose scores come from the NVFP4 Q and K;
  *                   probabilities and V stay BF16.
  *   attn_bwd_bf16   gradients of attn_fwd_bf16 with respect to Q, K and V.
+ *   attn_bwd_fp4qk  training-time gradients of attn_fwd_fp4qk (straight-
+ *                   through quantizer), with respect to the original Q, K, V.
  *
  * The method is the one of "Pika H3 Flex in FastVideo: 7x Faster, and Near
  * Real Time in 4-bit" (haoailab blog): section "Faster at BF16" (dense
@@ -192,6 +194,43 @@ int attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   uint16_t* dq, uint16_t* dk, uint16_t* dv,
                   void* workspace, size_t workspace_bytes,
                   int H, int L, int d, float softmax_scale, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd_fp4qk needs (0 on a bad shape):
+ * 4 * H * L * d * 2 + 2 * H * L * 4 (dequantized Q, K and their gradients in
+ * BF16, and the row statistics).
+ */
+size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d);
+
+/*
+ * attn_bwd_fp4qk - training-time gradients of attn_fwd_fp4qk, with the NVFP4
+ * quantizer passed straight through (its gradient taken as the identity).
+ *   q_codes, q_scales, k_codes, k_scales : as written by qk_prep_fp4(_ex).
+ *   v, o, lse : the forward's V (BF16) and the output and natural-log LSE
+ *             written by attn_fwd_fp4qk (lse required).
+ *   dout      : [H, L, d] BF16, the gradient of the loss with respect to o.
+ *   dq, dk    : [H, L, d] BF16, written: gradients with respect to the
+ *             ORIGINAL Q and K (before smoothing and rotation).
+ *   dv        : [H, L, d] BF16, written.
+ *   flags     : the flags the codes were prepared with (LSD_PREP_ROTATE
+ *             decides whether dQ, dK are rotated back; LSD_PREP_SMOOTH_K is
+ *             accepted and changes nothing, see below); other bits ->
+ *             LSD_ERR_FLAGS.
+ *   workspace : at least attn_bwd_fp4qk_workspace_bytes bytes, 256-aligned.
+ * Computes the attn_bwd_bf16 gradients at the exactly dequantized Q, K (in
+ * the rotated basis) and then dQ = dQh R, dK = dKh R with R = H / sqrt(128)
+ * (symmetric, orthonormal).  The Jacobian of the mean-key subtraction is
+ * omitted: it would subtract the mean over keys of dK, which is zero because
+ * softmax ignores a shift shared by every key (only rounding would change).
+ * Source: "NVFP4 QAD" (distillation with the deployed numerics in the loop)
+ * and "FP4 attention" (the training-time FP4 attention).
+ */
+int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales,
+                   const uint8_t* k_codes, const uint8_t* k_scales,
+                   const uint16_t* v, const uint16_t* o, const float* lse,
+                   const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int H, int L, int d, float softmax_scale, int flags, void* stream);
 
 #ifdef __cplusplus
 }

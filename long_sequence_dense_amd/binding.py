@@ -38,6 +38,8 @@ SIGNATURES = {
     "attn_fwd_fp4qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
     "attn_bwd_bf16_workspace_bytes": (_S, [_I, _I, _I]),
     "attn_bwd_bf16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _F, _P]),
+    "attn_bwd_fp4qk_workspace_bytes": (_S, [_I, _I, _I]),
+    "attn_bwd_fp4qk": (_I, [_P] * 12 + [_S, _I, _I, _I, _F, _I, _P]),
 }
 
 _lib = None
@@ -234,4 +236,38 @@ def attn_bwd_bf16(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, softmax_scal
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), H, L, d, scale, _stream(stream))
     _check("attn_bwd_bf16", st)
+    return tuple(outs)
+
+
+def attn_bwd_fp4qk_workspace_bytes(H, L, d=HEAD_DIM):
+    return int(load_library().attn_bwd_fp4qk_workspace_bytes(H, L, d))
+
+
+def attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, dout, dq=None, dk=None, dv=None,
+                   softmax_scale=None, flags=PREP_SMOOTH_K | PREP_ROTATE, workspace=None, stream=None):
+    """Straight-through gradients (dq, dk, dv) of attn_fwd_fp4qk with respect
+    to the original Q, K and V; o and lse are the FP4-QK forward's outputs."""
+    import torch
+    H, L, d = v.shape
+    for n, t in (("v", v), ("o", o), ("dout", dout)):
+        _need(t, n, _bf16_types(), (H, L, d))
+    for n, t in (("q_codes", q_codes), ("k_codes", k_codes)):
+        _need(t, n, (torch.uint8,), (H, L, d // 2))
+    for n, t in (("q_scales", q_scales), ("k_scales", k_scales)):
+        _need(t, n, (torch.uint8,), (H, L, d // 16))
+    _need(lse, "lse", (torch.float32,), (H, L))
+    outs = []
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty((H, L, d), dtype=torch.bfloat16, device=v.device)
+        _need(t, n, _bf16_types(), (H, L, d))
+        outs.append(t)
+    if workspace is None:
+        workspace = torch.empty(attn_bwd_fp4qk_workspace_bytes(H, L, d), dtype=torch.uint8, device=v.device)
+    scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    st = load_library().attn_bwd_fp4qk(
+        _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+        _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        H, L, d, scale, int(flags), _stream(stream))
+    _check("attn_bwd_fp4qk", st)
     return tuple(outs)

@@ -134,4 +134,32 @@ int attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
                                             (hipStream_t)stream));
 }
 
+size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d) {
+  if (check_shape(H, L, d) != LSD_OK) return 0;
+  return lsd::attn_bwd_fp4qk_workspace_bytes(H, L);
+}
+
+int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                   const uint8_t* k_scales, const uint16_t* v, const uint16_t* o, const float* lse,
+                   const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
+                   size_t workspace_bytes, int H, int L, int d, float softmax_scale, int flags, void* stream) {
+  int st = check_shape(H, L, d);
+  if (st != LSD_OK) return st;
+  if ((st = check_attn_len(L)) != LSD_OK) return st;
+  if (flags & ~(LSD_PREP_SMOOTH_K | LSD_PREP_ROTATE)) return LSD_ERR_FLAGS;
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return LSD_ERR_NULL;
+  if (!aligned16(q_codes) || !aligned16(q_scales) || !aligned16(k_codes) || !aligned16(k_scales) ||
+      !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      ((uintptr_t)lse & 3u))
+    return LSD_ERR_ALIGN;
+  if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lsd::attn_bwd_fp4qk_workspace_bytes(H, L))
+    return LSD_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, dout, dq, dk, dv,
+                                                  workspace, H, L, softmax_scale, (flags & LSD_PREP_ROTATE) != 0,
+                                                  (hipStream_t)stream));
+}
+
 }  // extern "C"

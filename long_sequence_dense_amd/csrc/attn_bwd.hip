@@ -477,9 +477,95 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
   }
 }
 
+// ------------------------------------------------- training-time FP4 QK --
+//
+// Gradients of the FP4-QK forward with the quantizer passed straight through
+// (the usual quantization-aware-training choice; the pages train with the
+// deployed FP4 attention in the loop, "NVFP4 QAD" and "FP4 attention"): the
+// BF16 backward above evaluated at the dequantized Q, K (exact in BF16), then
+// dQ and dK rotated back by the same orthonormal Hadamard matrix (it is
+// symmetric and its own inverse).  The mean subtraction's Jacobian
+// (I - 11^T / L on dK) is left out: the key-side gradient of attention sums to
+// zero over keys, so it would remove only rounding.
+
+constexpr int DEQ_THREADS = 256;               // one 16-channel block per thread
+
+__global__ __launch_bounds__(DEQ_THREADS) void fp4_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                                 const uint8_t* __restrict__ scales,
+                                                                 uint16_t* __restrict__ out, long long nblocks) {
+  const long long i = (long long)blockIdx.x * DEQ_THREADS + threadIdx.x;
+  if (i >= nblocks) return;
+  const u32x2 c = *(const u32x2*)(codes + 8 * i);
+  const float sc = e4m3_to_f32(scales[i]);
+  *(u16x8*)(out + 16 * i) = dequant8(c[0], sc);
+  *(u16x8*)(out + 16 * i + 8) = dequant8(c[1], sc);
+}
+
+constexpr int ROT_THREADS = 256;               // four lanes per row, 64 rows per workgroup
+constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;  // RN32(1/sqrt(128))
+
+__device__ __forceinline__ float quad_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
+// y = x H / sqrt(128) per 128-channel BF16 row, in fp32, rounded to BF16:
+// lane p of a quad holds channels 32 p .. +31; butterfly stages 0-4 in
+// registers, 5-6 across the quad.
+__global__ __launch_bounds__(ROT_THREADS) void rotate_rows_kernel(const uint16_t* __restrict__ in,
+                                                                 uint16_t* __restrict__ out, long long nrows) {
+  const int tid = threadIdx.x;
+  const int part = tid & 3;
+  const long long row = (long long)blockIdx.x * (ROT_THREADS / 4) + (tid >> 2);
+  if (row >= nrows) return;                    // whole quads leave together
+  const uint16_t* rp = in + row * kHeadDim + 32 * part;
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 w = *(const u32x4*)(rp + 8 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < 5; ++st) {
+    const int hs = 1 << st;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & hs) == 0) {
+        const float a = x[i], b = x[i + hs];
+        x[i] = a + b;
+        x[i + hs] = a - b;
+      }
+    }
+  }
+  const float k5 = (part & 1) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], k5, quad_xor1(x[i]));
+  const float k6 = (part & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = __builtin_fmaf(x[i], k6, quad_xor2(x[i]));
+  uint16_t* op = out + row * kHeadDim + 32 * part;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u16x8 w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = f32_to_bf16_rne(x[8 * i + j] * kInvSqrt128);
+    *(u16x8*)(op + 8 * i) = w;
+  }
+}
+
 }  // namespace
 
 size_t attn_bwd_workspace_bytes(int H, int L) { return (size_t)2 * H * (size_t)L * sizeof(float); }
+
+size_t attn_bwd_fp4qk_workspace_bytes(int H, int L) {
+  return (size_t)4 * H * (size_t)L * kHeadDim * 2 + attn_bwd_workspace_bytes(H, L);
+}
 
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                            const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
@@ -504,6 +590,32 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   const long long nq = (long long)b.n_qtiles * H;
   if (nq > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)nq), dim3(DQ_THREADS), 0, stream, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                                 const uint16_t* v, const uint16_t* o, const float* lse, const uint16_t* dout,
+                                 uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, int H, int L, float scale,
+                                 bool rotate, hipStream_t stream) {
+  const long long nrows = (long long)H * L;
+  const size_t elems = (size_t)nrows * kHeadDim;
+  uint16_t* qh = (uint16_t*)ws;                // workspace: Qh, Kh, dQh, dKh (BF16), then the row statistics
+  uint16_t* kh = qh + elems;
+  uint16_t* dqh = kh + elems;
+  uint16_t* dkh = dqh + elems;
+  void* stats = dkh + elems;
+  const long long nblocks = nrows * (kHeadDim / kBlock);
+  const unsigned db = (unsigned)((nblocks + DEQ_THREADS - 1) / DEQ_THREADS);
+  hipLaunchKernelGGL(fp4_dequant_kernel, dim3(db), dim3(DEQ_THREADS), 0, stream, qc, qs, qh, nblocks);
+  hipLaunchKernelGGL(fp4_dequant_kernel, dim3(db), dim3(DEQ_THREADS), 0, stream, kc, ks, kh, nblocks);
+  hipError_t e = launch_attn_bwd(qh, kh, v, o, lse, dout, rotate ? dqh : dq, rotate ? dkh : dk, dv, stats, H, L,
+                                 scale, stream);
+  if (e != hipSuccess) return e;
+  if (rotate) {
+    const unsigned rb = (unsigned)((nrows + (ROT_THREADS / 4) - 1) / (ROT_THREADS / 4));
+    hipLaunchKernelGGL(rotate_rows_kernel, dim3(rb), dim3(ROT_THREADS), 0, stream, dqh, dq, nrows);
+    hipLaunchKernelGGL(rotate_rows_kernel, dim3(rb), dim3(ROT_THREADS), 0, stream, dkh, dk, nrows);
+  }
   return hipGetLastError();
 }
 

@@ -88,31 +88,6 @@ struct Smem {
   uint16_t v[2][BC * VS];
 };
 
-// Two FP4 codes (byte J of w) decoded exactly by the hardware (unit scale),
-// times the block scale s.
-template <int J>
-__device__ __forceinline__ void fp4_pair(uint32_t w, float s, float* f) {
-  const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, J);
-  f[2 * J] = a[0] * s;
-  f[2 * J + 1] = a[1] * s;
-}
-
-// 8 codes (one dword, low nibble first) times scale s -> 8 BF16 bit patterns.
-// Every product E2M1 x E4M3 has at most 6 significant bits and lies in
-// [2^-10, 2688], so the float32 product is exact and truncating it to BF16 is
-// exact.
-__device__ __forceinline__ u16x8 dequant8(uint32_t w, float s) {
-  float f[8];
-  fp4_pair<0>(w, s, f);
-  fp4_pair<1>(w, s, f);
-  fp4_pair<2>(w, s, f);
-  fp4_pair<3>(w, s, f);
-  u16x8 r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (uint16_t)(__float_as_uint(f[j]) >> 16);
-  return r;
-}
-
 // 16 NVFP4 values (8 code bytes + 1 scale byte) to 16 BF16 bit patterns.
 __device__ __forceinline__ void dequant16(uint64_t codes, uint32_t scale_byte, u16x8& lo, u16x8& hi) {
   const float s = e4m3_to_f32(scale_byte);

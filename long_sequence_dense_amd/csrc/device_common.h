@@ -33,4 +33,29 @@ __device__ __forceinline__ uint32_t e2m1_to_f32_bits(uint32_t code) {
   return mag | ((code & 8u) << 28);
 }
 
+// Two FP4 codes (byte J of w) decoded exactly by the hardware (unit scale),
+// times the block scale s.
+template <int J>
+__device__ __forceinline__ void fp4_pair(uint32_t w, float s, float* f) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, J);
+  f[2 * J] = a[0] * s;
+  f[2 * J + 1] = a[1] * s;
+}
+
+// 8 codes (one dword, low nibble first) times scale s -> 8 BF16 bit patterns.
+// Every product E2M1 x E4M3 has at most 6 significant bits and lies in
+// [2^-10, 2688], so the float32 product is exact and truncating it to BF16 is
+// exact.
+__device__ __forceinline__ u16x8 dequant8(uint32_t w, float s) {
+  float f[8];
+  fp4_pair<0>(w, s, f);
+  fp4_pair<1>(w, s, f);
+  fp4_pair<2>(w, s, f);
+  fp4_pair<3>(w, s, f);
+  u16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (uint16_t)(__float_as_uint(f[j]) >> 16);
+  return r;
+}
+
 }  // namespace lsd

@@ -23,6 +23,12 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                            void* ws, int H, int L, float scale, hipStream_t stream);
 
+size_t attn_bwd_fp4qk_workspace_bytes(int H, int L);
+hipError_t launch_attn_bwd_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                                 const uint16_t* v, const uint16_t* o, const float* lse, const uint16_t* dout,
+                                 uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, int H, int L, float scale,
+                                 bool rotate, hipStream_t stream);
+
 // Q/K preparation (qk_prep.hip)
 size_t prep_workspace_bytes(int H, int L);
 hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uint8_t* qs,

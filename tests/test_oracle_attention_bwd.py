@@ -38,6 +38,13 @@ def finite_diff(q, k, v, do, scale, which, h=1e-6):
     return g
 
 
+def sylvester(n):
+    h = np.array([[1]], dtype=np.int64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
 def tiny(seed, H=1, L=5, d=8):
     rng = np.random.default_rng(seed)
     return [rng.standard_normal((H, L, d)) for _ in range(4)]
@@ -115,3 +122,67 @@ def test_planted_mistakes_fail():
     for w in wrong:
         assert np.max(np.abs(w - fdq[0])) > 1e-3
     assert np.max(np.abs(scale * good @ q[0] - fdk[0])) > 1e-3   # dS instead of dS^T for dK
+
+
+# ---- training-time FP4-QK gradients (straight-through quantizer) -------------
+
+def test_fp4_ste_equals_plain_gradient_when_quantization_is_exact():
+    # Values NVFP4 holds exactly (E2M1 x E4M3, a +-6 in every block), no
+    # transforms: the straight-through gradient is the plain gradient.
+    from oracle import nvfp4
+    from oracle.attention_bwd import fp4qk_bwd_ste_fp64
+    rng = np.random.default_rng(9)
+    e2 = nvfp4.e2m1_decode_table()
+    e4 = nvfp4.e4m3_decode_table()
+
+    def grid(n):
+        sc = rng.integers(0x28, 0x38, (1, n, 8))
+        cd = rng.integers(0, 16, (1, n, 128))
+        cd[..., ::16] = rng.choice([7, 15], (1, n, 8))
+        return e2[cd] * np.repeat(e4[sc], 16, axis=-1)
+
+    q, k = grid(24), grid(24)
+    v, do = rng.standard_normal((1, 24, 128)), rng.standard_normal((1, 24, 128))
+    bits = lambda x: (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    prep = nvfp4.qk_prep_fp4(bits(q), bits(k), smooth=False, rotate=False)
+    got = fp4qk_bwd_ste_fp64(prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], v, do, 0.05,
+                             rotate=False, smooth=False)
+    want = attention_bwd_fp64(q, k, v, do, 0.05)
+    for g, w in zip(got, want):
+        assert np.max(np.abs(g - w)) <= 1e-12 * (1 + np.max(np.abs(w)))
+
+
+def test_fp4_ste_rotation_and_mean_terms():
+    # The rotation is undone by the same orthonormal matrix (it is symmetric),
+    # and the mean subtraction's Jacobian is I - 11^T / L, checked here by
+    # finite differences of the linear map K -> K - mean(K) composed with the
+    # rotation; the attention gradient itself sums to zero over keys, so the
+    # mean term only removes rounding.
+    from oracle import nvfp4
+    from oracle.attention_bwd import fp4qk_bwd_ste_fp64
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((1, 20, 128)).astype(np.float32)
+    k = (rng.standard_normal((1, 20, 128)) + 2.0).astype(np.float32)
+    bits = lambda x: (x.view(np.uint32) >> 16).astype(np.uint16)
+    prep = nvfp4.qk_prep_fp4(bits(q), bits(k))
+    v, do = rng.standard_normal((1, 20, 128)), rng.standard_normal((1, 20, 128))
+    dq, dk, dv = fp4qk_bwd_ste_fp64(prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], v, do, 0.1)
+    qh = nvfp4.dequant_nvfp4(prep["q_codes"], prep["q_scales"])
+    kh = nvfp4.dequant_nvfp4(prep["k_codes"], prep["k_scales"])
+    dqh, dkh, dv2 = attention_bwd_fp64(qh, kh, v, do, 0.1)
+    hm = sylvester(128) / math.sqrt(128)
+    assert np.max(np.abs(hm @ hm - np.eye(128))) <= 1e-12
+    assert np.max(np.abs(dq @ hm - dqh)) <= 1e-12 * np.max(np.abs(dqh))     # rotating back recovers dQh
+    assert np.array_equal(dv, dv2)
+    # chain rule through f(K) = (K - mean(K)) R by finite differences of a
+    # linear functional <G, f(K)> with G = dKh
+    g = dkh[0]
+    f = lambda kk: float((g * ((kk - kk.mean(axis=0, keepdims=True)) @ hm)).sum())
+    k0 = rng.standard_normal((20, 128))
+    fd = np.zeros_like(k0)
+    for idx in [(0, 0), (3, 17), (19, 127), (7, 64)]:
+        e = np.zeros_like(k0)
+        e[idx] = 1e-3
+        fd[idx] = (f(k0 + e) - f(k0 - e)) / 2e-3
+        assert abs(fd[idx] - dk[0][idx]) <= 1e-9 * (1 + abs(dk[0][idx]))
+    assert np.max(np.abs(dkh.sum(axis=1))) <= 1e-12 * np.abs(dkh).sum()
