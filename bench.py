@@ -57,16 +57,21 @@ def gen_inputs(torch, name):
     return cfg, out
 
 
+KERNEL_SOURCES = ("attn_fwd.hip", "device_common.h", "lsd_internal.h")
+
+
 def kernel_source_hash():
-    """sha256 of the attention kernel source with comments and blank lines
-    removed: counter-derived traffic is only reported for the code it was
-    measured on."""
+    """sha256 of the attention kernel's sources (the kernel file and the
+    headers it includes) with comments and blank lines removed:
+    counter-derived traffic is only reported for the code it was measured on."""
     import hashlib
     import re
-    src = os.path.join(ROOT, "long_sequence_dense_amd", "csrc", "attn_fwd.hip")
-    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in open(src).read().splitlines())
-    code = "\n".join(ln for ln in lines if ln)
-    return hashlib.sha256(code.encode()).hexdigest()
+    code = []
+    for name in KERNEL_SOURCES:
+        src = os.path.join(ROOT, "long_sequence_dense_amd", "csrc", name)
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in open(src).read().splitlines())
+        code.append("\n".join(ln for ln in lines if ln))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()
 
 
 def stored_traffic():

@@ -58,11 +58,11 @@ constexpr int NLD = KCHUNKS / NTHREADS;            // chunks per thread per tile
 constexpr int NLD4 = BC * (kHeadDim / kBlock) / NTHREADS;   // FP4 blocks per thread per tile
 constexpr int KS = kHeadDim + 8;        // K row stride in LDS (bf16): 272 B
 constexpr int VS = kHeadDim + 32;       // V row stride in LDS (bf16): 320 B
-constexpr float kSumBound = 65536.0f;
+constexpr float kSumBound = 65536.0f;   // largest per-lane tile sum accepted without recomputing the max
 #ifndef LSD_ATTN_KPRE
 #define LSD_ATTN_KPRE 4
 #endif
-constexpr int KPRE = LSD_ATTN_KPRE;     // K operands of the next tile read during the P.V half   // largest per-lane tile sum accepted without recomputing the max
+constexpr int KPRE = LSD_ATTN_KPRE;     // K operands of the next tile read during the P.V half
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
