@@ -110,3 +110,48 @@ def test_fp4qk_argument_errors(lib):
 def test_missing_library_raises(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         binding.load_library(str(tmp_path / "nope.so"))
+
+
+def test_bwd_workspace_queries(lib):
+    assert lib.attn_bwd_bf16_workspace_bytes(40, 109000, 128) == 2 * 40 * 109000 * 4
+    assert lib.attn_bwd_bf16_workspace_bytes(2, 16, 64) == 0
+    assert lib.attn_bwd_fp4qk_workspace_bytes(2, 16, 128) == 4 * 2 * 16 * 128 * 2 + 2 * 2 * 16 * 4
+    assert lib.attn_bwd_fp4qk_workspace_bytes(0, 16, 128) == 0
+
+
+def test_bwd_bf16_argument_errors(lib):
+    f = lib.attn_bwd_bf16
+    ws = ctypes.c_void_p(0x200000)
+    need = lib.attn_bwd_bf16_workspace_bytes(2, 16, 128)
+    ok = [A] * 9
+    assert f(*ok, ws, need, 2, 16, 64, 0.1, N) == 3                     # d
+    assert f(*ok, ws, need, 2, 1 << 23, 128, 0.1, N) == 2               # one head too long
+    for i in range(9):                                                   # every pointer is required
+        args = list(ok)
+        args[i] = N
+        assert f(*args, ws, need, 2, 16, 128, 0.1, N) == 1, i
+    args = list(ok)
+    args[4] = ctypes.c_void_p(0x100002)                                  # lse only needs 4-byte alignment
+    assert f(*args, ws, need, 2, 16, 128, 0.1, N) == 4
+    args[4] = ctypes.c_void_p(0x100004)
+    args[6] = B                                                          # dq misaligned
+    assert f(*args, ws, need, 2, 16, 128, 0.1, N) == 4
+    assert f(*ok, ws, need, 2, 16, 128, 0.0, N) == 7                    # scale
+    assert f(*ok, N, need, 2, 16, 128, 0.1, N) == 5                     # workspace
+    assert f(*ok, ws, need - 1, 2, 16, 128, 0.1, N) == 5
+
+
+def test_bwd_fp4qk_argument_errors(lib):
+    f = lib.attn_bwd_fp4qk
+    ws = ctypes.c_void_p(0x200000)
+    need = lib.attn_bwd_fp4qk_workspace_bytes(2, 16, 128)
+    ok = [A] * 11
+    assert f(*ok, ws, need, 2, 16, 128, 0.1, 4, N) == 8                 # unknown flag bit
+    assert f(*ok, ws, need, 2, 16, 256, 0.1, 3, N) == 3
+    for i in range(11):
+        args = list(ok)
+        args[i] = N
+        assert f(*args, ws, need, 2, 16, 128, 0.1, 3, N) == 1, i
+    assert f(*ok, ws, need, 2, 16, 128, float("nan"), 3, N) == 7
+    assert f(*ok, ws, need - 1, 2, 16, 128, 0.1, 3, N) == 5
+    assert f(*ok, ctypes.c_void_p(0x200010), need, 2, 16, 128, 0.1, 3, N) == 5
