@@ -14,7 +14,10 @@ Contents
                       variants (no smoothing, no rotation).
 ``oracle.fp4_error``  relative attention error of the FP4-QK variants against
                       exact attention.
-``oracle.attention_bwd`` fp64 gradients of attention (dQ, dK, dV).
+``oracle.attention_bwd`` fp64 gradients of attention (dQ, dK, dV), and of the
+                      FP4-QK attention with a straight-through quantizer.
+``oracle.nvfp4_linear``  NVFP4 W4A4 linear layer (quantizer with a global
+                      scale, exact product).
 
 Source: "Pika H3 Flex in FastVideo: 7x Faster, and Near Real Time in 4-bit"
 (haoailab blog), sections "Faster at BF16" and "FP4 attention".  Every function
