@@ -13,6 +13,9 @@
  *   attn_bwd_bf16   gradients of attn_fwd_bf16 with respect to Q, K and V.
  *   attn_bwd_fp4qk  training-time gradients of attn_fwd_fp4qk (straight-
  *                   through quantizer), with respect to the original Q, K, V.
+ *   nvfp4_quantize  NVFP4 quantization (per-tensor global scale) of the rows
+ *                   of a linear layer's activation or weight matrix.
+ *   nvfp4_linear    the W4A4 linear layer Y = X W^T from two such operands.
  *
  * The method is the one of "Pika H3 Flex in FastVideo: 7x Faster, and Near
  * Real Time in 4-bit" (haoailab blog): section "Faster at BF16" (dense
@@ -58,12 +61,12 @@ enum lsd_status {
   LSD_ERR_ALIGN = 4,          /* a tensor pointer is not 16-byte aligned      */
   LSD_ERR_WORKSPACE = 5,      /* workspace missing, misaligned or too small   */
   LSD_ERR_LAUNCH = 6,         /* the HIP runtime rejected a kernel launch     */
-  LSD_ERR_SCALE = 7,          /* softmax_scale is not finite and positive     */
+  LSD_ERR_SCALE = 7,          /* a scale argument is not finite and positive  */
   LSD_ERR_FLAGS = 8           /* unknown bits in a flags argument             */
 };
 
 /* Version of this ABI (the value of LSD_ABI_VERSION the library was built with). */
-#define LSD_ABI_VERSION 2
+#define LSD_ABI_VERSION 3
 int lsd_abi_version(void);
 
 /* Static description of a status code ("ok", "null pointer", ...). */
@@ -231,6 +234,51 @@ int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales,
                    const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                    void* workspace, size_t workspace_bytes,
                    int H, int L, int d, float softmax_scale, int flags, void* stream);
+
+/*
+ * nvfp4_quantize - NVFP4 codes of a row-major [rows, cols] BF16 matrix (an
+ * activation X or a weight W of a linear layer).
+ *   x       : [rows, cols] BF16 bits, read only, 16-byte aligned.
+ *   codes   : [rows, cols / 2] bytes, written; byte j of a row holds value
+ *             2j in its low nibble and 2j+1 in its high nibble (E2M1: sign
+ *             bit 3, magnitude index 0..7 for 0, .5, 1, 1.5, 2, 3, 4, 6).
+ *             16-byte aligned.
+ *   scales  : [rows, cols / 16] E4M3 codes (one per 16 consecutive values of
+ *             a row), written.
+ *   rows >= 1, cols >= 16 and a multiple of 16, rows * cols / 16 < 2^31 * 256
+ *   (else LSD_ERR_SHAPE).
+ *   global_scale : g, float32, finite, > 0 and with a finite float32 1/g
+ *             (else LSD_ERR_SCALE).  The quantizer sees x' = RN32(x * RN32(1/g))
+ *             and quantizes each block of 16 as qk_prep_fp4 does (E4M3 scale
+ *             of amax / 6 rounded to nearest even, then each value divided by
+ *             it and rounded to nearest even E2M1, saturating at 6); a code e
+ *             with block scale s stands for e * s * g, so g sets the clipping
+ *             level 6 * 448 * g.  g is not stored: pass it to nvfp4_linear.
+ * Source: "NVFP4 QAD" (4-bit weights and activations in every attention and
+ * feed-forward linear, one 8-bit scale per 16 values; static activation
+ * scales from calibration) with the block format of "FP4 attention".
+ */
+int nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long rows, int cols,
+                   float global_scale, void* stream);
+
+/*
+ * nvfp4_linear - Y = (X^ g_x) (W^ g_w)^T, the W4A4 linear layer.
+ *   x_codes, x_scales : the activation, [M, K] quantized by nvfp4_quantize
+ *                       with global scale x_global_scale.
+ *   w_codes, w_scales : the weight, [N, K] (one row per output feature),
+ *                       quantized with global scale w_global_scale.
+ *   y       : [M, N] BF16 bits, written (round to nearest even).
+ *   M >= 1, N >= 1, K >= 16 and a multiple of 16, K <= 2^20 (else
+ *   LSD_ERR_SHAPE); the scales must be finite and > 0 (else LSD_ERR_SCALE);
+ *   code pointers 16-byte aligned, y 8-byte aligned (else LSD_ERR_ALIGN).
+ * Both operands are dequantized exactly to BF16 on chip (an E2M1 value times
+ * an E4M3 scale fits BF16), their products accumulate in fp32 on the matrix
+ * cores, the fp32 sum is multiplied by RN32(g_x * g_w) and rounded to BF16.
+ * No bias, no activation function.
+ */
+int nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, float x_global_scale,
+                 const uint8_t* w_codes, const uint8_t* w_scales, float w_global_scale,
+                 uint16_t* y, int M, int N, int K, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,7 @@ SOURCES = {
     "attn_fwd.hip": ["-fno-honor-nans"],
     "attn_bwd.hip": ["-fno-honor-nans"],
     "qk_prep.hip": ["-ffp-contract=off"],
+    "nvfp4_gemm.hip": [],
 }
 
 

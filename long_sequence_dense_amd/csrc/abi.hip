@@ -43,7 +43,7 @@ const char* lsd_status_str(int status) {
     case LSD_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case LSD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case LSD_ERR_LAUNCH: return "kernel launch failed";
-    case LSD_ERR_SCALE: return "softmax_scale must be finite and > 0";
+    case LSD_ERR_SCALE: return "scale must be finite and > 0";
     case LSD_ERR_FLAGS: return "unknown flag bits";
     default: return "unknown status";
   }
@@ -160,6 +160,30 @@ int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
   return launch_status(lsd::launch_attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, dout, dq, dk, dv,
                                                   workspace, H, L, softmax_scale, (flags & LSD_PREP_ROTATE) != 0,
                                                   (hipStream_t)stream));
+}
+
+int nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long rows, int cols,
+                   float global_scale, void* stream) {
+  if (rows < 1 || cols < lsd::kBlock || cols % lsd::kBlock) return LSD_ERR_SHAPE;
+  if (rows > (LLONG_MAX / cols) || rows * (cols / lsd::kBlock) >= (1LL << 39)) return LSD_ERR_SHAPE;
+  if (!x || !codes || !scales) return LSD_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes)) return LSD_ERR_ALIGN;
+  if (check_scale(global_scale) != LSD_OK || !std::isfinite((float)(1.0 / (double)global_scale)))
+    return LSD_ERR_SCALE;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_nvfp4_quantize(x, codes, scales, rows, cols, global_scale, (hipStream_t)stream));
+}
+
+int nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, float x_global_scale,
+                 const uint8_t* w_codes, const uint8_t* w_scales, float w_global_scale,
+                 uint16_t* y, int M, int N, int K, void* stream) {
+  if (M < 1 || N < 1 || K < lsd::kBlock || K % lsd::kBlock || K > (1 << 20)) return LSD_ERR_SHAPE;
+  if (!x_codes || !x_scales || !w_codes || !w_scales || !y) return LSD_ERR_NULL;
+  if (!aligned16(x_codes) || !aligned16(w_codes) || ((uintptr_t)y & 7u)) return LSD_ERR_ALIGN;
+  if (check_scale(x_global_scale) != LSD_OK || check_scale(w_global_scale) != LSD_OK) return LSD_ERR_SCALE;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_nvfp4_linear(x_codes, x_scales, x_global_scale, w_codes, w_scales,
+                                                w_global_scale, y, M, N, K, (hipStream_t)stream));
 }
 
 }  // extern "C"

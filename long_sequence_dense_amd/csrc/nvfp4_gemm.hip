@@ -1,0 +1,215 @@
+// NVFP4 W4A4 linear layer on gfx950 (MI355X): Y = (X^ g_x)(W^ g_w)^T.
+//
+// Method: "Pika H3 Flex in FastVideo: 7x Faster, and Near Real Time in 4-bit",
+// section "NVFP4 QAD": every attention and feed-forward linear runs with 4-bit
+// weights and activations, one 8-bit scale per 16 values (the block format of
+// section "FP4 attention": E2M1 values, an E4M3 scale per 16 consecutive
+// values along K), plus one fp32 global scale per tensor.
+//
+// gfx950's scaled MFMA takes power-of-two (E8M0) scales per 32 values; an
+// E4M3 scale per 16 values cannot be folded into it.  E2M1 x E4M3 products
+// have at most 6 significant bits, so they are exact in BF16: both operands
+// are dequantized exactly while they are staged into LDS and multiplied on the
+// 32x32x16 BF16 MFMA with fp32 accumulation; the product of the two global
+// scales is applied to the fp32 result, which is rounded to BF16.
+//
+// Tiling: a workgroup computes a 256 (tokens m) x 256 (features n) tile of Y
+// as Y^T blocks (W rows are the A operand, X rows the B operand, so that a
+// lane's accumulator holds four consecutive features of one token); eight
+// waves (two per SIMD) of 128 (n) x 64 (m), i.e. 4 x 2 blocks of 32 x 32.  K
+// advances 64 at a time through double-buffered LDS tiles (row stride 144 B:
+// the operand reads are free of bank conflicts); the codes of the next stage
+// are loaded into registers while the current one is multiplied.  Workgroups
+// are numbered so that consecutive ones share the X rows and each XCD (own L2)
+// takes a contiguous range.  Rows past M or N and blocks past K load as zeros;
+// rows past M or N are not stored.
+#include "lsd_internal.h"
+#include "device_common.h"
+
+namespace lsd {
+namespace {
+
+constexpr int GM = 256;                 // tokens (rows of Y) per workgroup
+constexpr int GN = 256;                 // features (columns of Y) per workgroup
+constexpr int GK = 64;                  // K per LDS stage
+constexpr int GT = 512;                 // threads per workgroup
+constexpr int GS = GK + 8;              // LDS row stride (bf16)
+constexpr int NB = GK / kBlock;         // 16-value blocks per row per stage
+constexpr int SB = (GN * NB) / GT;      // blocks of one operand staged per thread per stage
+constexpr int kOutside = 0x7FFFFFF0;    // a byte offset past every buffer range (loads return 0)
+
+struct GemmParams {
+  const uint8_t* xc;
+  const uint8_t* xs;
+  const uint8_t* wc;
+  const uint8_t* ws;
+  uint16_t* y;
+  int M, N, K;
+  int tiles_n, tiles;
+  float gscale;                         // g_x * g_w
+};
+
+struct GemmSmem {
+  uint16_t w[2][GN * GS];
+  uint16_t x[2][GM * GS];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long long bytes) {
+  const int n = bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Codes and scales of one operand's stage, this thread's share: block id
+// b = tid + GT * i covers row b / NB, values 16 * (b % NB) .. +15 of the stage.
+struct Stage {
+  u32x2 c[SB];
+  uint32_t s[SB];
+};
+
+__device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int K, int k0,
+                                           int tid, Stage& st) {
+#pragma unroll
+  for (int i = 0; i < SB; ++i) {
+    const int b = tid + GT * i;
+    const int row = b / NB, kb = b % NB;
+    // blocks past K (a ragged last stage) read beyond the buffer range: zeros
+    const bool in = k0 + kBlock * kb < K;
+    const int oc = in ? row * (K / 2) + k0 / 2 + 8 * kb : kOutside;
+    const int os = in ? row * (K / kBlock) + k0 / kBlock + kb : kOutside;
+    st.c[i] = __builtin_amdgcn_raw_buffer_load_b64(rc, oc, 0, 0);
+    st.s[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, os, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void store_stage(uint16_t* tile, int tid, const Stage& st) {
+#pragma unroll
+  for (int i = 0; i < SB; ++i) {
+    const int b = tid + GT * i;
+    const int row = b / NB, kb = b % NB;
+    const float sc = e4m3_to_f32(st.s[i] & 0xFF);
+    *(u16x8*)(tile + row * GS + 16 * kb) = dequant8(st.c[i][0], sc);
+    *(u16x8*)(tile + row * GS + 16 * kb + 8) = dequant8(st.c[i][1], sc);
+  }
+}
+
+__device__ __forceinline__ bf16x8 operand(const uint16_t* tile, int lane_off, int row0, int ks) {
+  return __builtin_bit_cast(bf16x8, *(const u16x8*)(tile + row0 * GS + lane_off + 16 * ks));
+}
+
+__global__ __launch_bounds__(GT, 1) void nvfp4_gemm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) GemmSmem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wn = wave >> 2, wm = wave & 3;          // wave tile: features 128 wn.., tokens 64 wm..
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int lane_off = l32 * GS + 8 * hf;
+
+  // XCD-aware numbering (hardware id % 8 = XCD), then m-major tiles.
+  const int nblk = gridDim.x, bid = blockIdx.x;
+  const int per = nblk >> 3, rem = nblk & 7, xcd = bid & 7;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
+  const int tm = logical / p.tiles_n, tn = logical - tm * p.tiles_n;
+  const int m0 = tm * GM, n0 = tn * GN;
+  const int K = p.K;
+
+  const long long xrows = p.M - m0 < GM ? p.M - m0 : GM;
+  const long long wrows = p.N - n0 < GN ? p.N - n0 : GN;
+  const __amdgpu_buffer_rsrc_t rxc = rsrc(p.xc + (size_t)m0 * (K / 2), xrows * (K / 2));
+  const __amdgpu_buffer_rsrc_t rxs = rsrc(p.xs + (size_t)m0 * (K / kBlock), xrows * (K / kBlock));
+  const __amdgpu_buffer_rsrc_t rwc = rsrc(p.wc + (size_t)n0 * (K / 2), wrows * (K / 2));
+  const __amdgpu_buffer_rsrc_t rws = rsrc(p.ws + (size_t)n0 * (K / kBlock), wrows * (K / kBlock));
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = (f32x16)0.0f;
+
+  const int nst = (K + GK - 1) / GK;
+  {
+    Stage sw, sx;
+    load_stage(rwc, rws, K, 0, tid, sw);
+    load_stage(rxc, rxs, K, 0, tid, sx);
+    store_stage(sm.w[0], tid, sw);
+    store_stage(sm.x[0], tid, sx);
+  }
+  __syncthreads();
+
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < nst;
+    Stage sw, sx;
+    if (more) {
+      load_stage(rwc, rws, K, (s + 1) * GK, tid, sw);
+      load_stage(rxc, rxs, K, (s + 1) * GK, tid, sx);
+    }
+    const uint16_t* wt = sm.w[buf];
+    const uint16_t* xt = sm.x[buf];
+#pragma unroll
+    for (int ks = 0; ks < GK / 16; ++ks) {
+      bf16x8 a[4], b[2];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) a[nb] = operand(wt, lane_off, 128 * wn + 32 * nb, ks);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) b[mb] = operand(xt, lane_off, 64 * wm + 32 * mb, ks);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+    }
+    if (more) {
+      store_stage(sm.w[buf ^ 1], tid, sw);
+      store_stage(sm.x[buf ^ 1], tid, sx);
+    }
+    __syncthreads();
+  }
+
+  // Y^T block (nb, mb): lane holds token m0 + 64 wm + 32 mb + l32 and, per
+  // group g, features n0 + 128 wn + 32 nb + 8 g + 4 hf .. +3.
+  const bool vec = (p.N & 3) == 0;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = m0 + 64 * wm + 32 * mb + l32;
+    if (m >= p.M) continue;
+    uint16_t* yrow = p.y + (size_t)m * p.N;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + 128 * wn + 32 * nb + 8 * g + 4 * hf;
+        if (n >= p.N) continue;
+        u16x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[j] = __builtin_bit_cast(uint16_t, (__bf16)(acc[nb][mb][4 * g + j] * p.gscale));
+        if (vec) {
+          *(u16x4*)(yrow + n) = w;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (n + j < p.N) yrow[n + j] = w[j];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_nvfp4_linear(const uint8_t* xc, const uint8_t* xs, float gx, const uint8_t* wc, const uint8_t* ws,
+                               float gw, uint16_t* y, int M, int N, int K, hipStream_t stream) {
+  GemmParams p = {};
+  p.xc = xc; p.xs = xs; p.wc = wc; p.ws = ws; p.y = y;
+  p.M = M; p.N = N; p.K = K;
+  p.tiles_n = (N + GN - 1) / GN;
+  const long long tiles = (long long)((M + GM - 1) / GM) * p.tiles_n;
+  if (tiles <= 0 || tiles > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  p.tiles = (int)tiles;
+  p.gscale = gx * gw;
+  hipLaunchKernelGGL(nvfp4_gemm_kernel, dim3((unsigned)tiles), dim3(GT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace lsd

@@ -98,6 +98,41 @@ __device__ __forceinline__ float dpp_xor2(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
 }
 
+// One 16-value block: its E4M3 scale code (nearest to max|y| / 6) and the
+// packed E2M1 codes of y / scale (value j in nibble j, low nibble first).
+__device__ __forceinline__ u32x2 quant_block16(float* y, uint32_t& scode) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2)
+    amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(y[i]), __builtin_fabsf(y[i + 1])));
+  const uint32_t sc = e4m3_scale_code(amax);
+  scode = sc;
+  const float s = e4m3_pos(sc);
+  const float rinv = sc ? (float)(1.0 / (double)s) : 0.0f;     // RN32(1/s)
+  // t = RN32(y / s): Markstein's correction from q0 = RN(y * RN(1/s)); the
+  // remainder fma(q0, s, -y) is exact.  Written so that t keeps the sign of
+  // y also when y is a signed zero, and t = +-0 when s = 0 (rinv = 0).
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float q0 = y[i] * rinv;
+    const float rr = __builtin_fmaf(q0, s, -y[i]);
+    t[i] = __builtin_fmaf(-rr, rinv, q0);
+  }
+  // E2M1 with round-to-nearest-even and saturation (unit scale).
+  u32x2 w;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    uint32_t acc = 0u;
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, t[8 * d + 0], t[8 * d + 1], 1.0f, 0);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, t[8 * d + 2], t[8 * d + 3], 1.0f, 1);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, t[8 * d + 4], t[8 * d + 5], 1.0f, 2);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, t[8 * d + 6], t[8 * d + 7], 1.0f, 3);
+    w[d] = acc;
+  }
+  return w;
+}
+
 // Four lanes per 128-channel row, 32 consecutive channels per lane.  grid:
 // (row blocks of one head, heads), one lane quad per row.  K (KMEAN):
 // x = RN32(k - mean) first.  ROT: the rotation (otherwise y = x).
@@ -175,43 +210,42 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_kernel(const uint16_t* __
     for (int i = 0; i < 32; ++i) x[i] = x[i] * kHadamardScale;
   }
 
+  u32x4 wv;
   uint32_t scode[2];
 #pragma unroll
   for (int blk2 = 0; blk2 < 2; ++blk2) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2)
-      amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(x[16 * blk2 + i]),
-                                                   __builtin_fabsf(x[16 * blk2 + i + 1])));
-    const uint32_t sc = e4m3_scale_code(amax);
-    scode[blk2] = sc;
-    const float s = e4m3_pos(sc);
-    const float rinv = sc ? (float)(1.0 / (double)s) : 0.0f;     // RN32(1/s)
-    // t = RN32(y / s): Markstein's correction from q0 = RN(y * RN(1/s)); the
-    // remainder fma(q0, s, -y) is exact.  Written so that t keeps the sign of
-    // y also when y is a signed zero, and t = +-0 when s = 0 (rinv = 0).
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float y = x[16 * blk2 + i];
-      const float q0 = y * rinv;
-      const float rr = __builtin_fmaf(q0, s, -y);
-      x[16 * blk2 + i] = __builtin_fmaf(-rr, rinv, q0);
-    }
-  }
-  // E2M1 with round-to-nearest-even and saturation (unit scale): channel 2j in
-  // the low nibble of byte j, 2j+1 in the high nibble.
-  u32x4 wv;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    uint32_t acc = 0u;
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, x[8 * d + 0], x[8 * d + 1], 1.0f, 0);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, x[8 * d + 2], x[8 * d + 3], 1.0f, 1);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, x[8 * d + 4], x[8 * d + 5], 1.0f, 2);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, x[8 * d + 6], x[8 * d + 7], 1.0f, 3);
-    wv[d] = acc;
+    const u32x2 c = quant_block16(x + 16 * blk2, scode[blk2]);
+    wv[2 * blk2] = c[0];
+    wv[2 * blk2 + 1] = c[1];
   }
   *(u32x4*)(codes + row * (kHeadDim / 2) + part * 16) = wv;
   *(uint16_t*)(scales + row * (kHeadDim / kBlock) + part * 2) = (uint16_t)(scode[0] | (scode[1] << 8));
+}
+
+// NVFP4 quantization of the rows of a linear layer's operand: thread i takes
+// values 16 i .. 16 i + 15 (one block of a row; rows are whole blocks), y =
+// RN32(x * r) with r = RN32(1 / g) for the tensor's global scale g, then the
+// block is quantized as above (no rotation).
+__global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_rows_kernel(const uint16_t* __restrict__ src,
+                                                                        uint8_t* __restrict__ codes,
+                                                                        uint8_t* __restrict__ scales,
+                                                                        long long nblocks, float r) {
+  const long long i = (long long)blockIdx.x * QUANT_THREADS + threadIdx.x;
+  if (i >= nblocks) return;
+  const u32x4* p = (const u32x4*)(src + 16 * i);
+  const u32x4 a = p[0], b = p[1];
+  float y[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    y[2 * j] = __uint_as_float(a[j] << 16) * r;
+    y[2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u) * r;
+    y[8 + 2 * j] = __uint_as_float(b[j] << 16) * r;
+    y[8 + 2 * j + 1] = __uint_as_float(b[j] & 0xFFFF0000u) * r;
+  }
+  uint32_t sc;
+  const u32x2 c = quant_block16(y, sc);
+  *(u32x2*)(codes + 8 * i) = c;
+  scales[i] = (uint8_t)sc;
 }
 
 // ---------------------------------------------------------------- mean -------
@@ -417,6 +451,17 @@ void launch_quant(const uint16_t* src, const float* kmean, uint8_t* codes, uint8
 }
 
 }  // namespace
+
+hipError_t launch_nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long rows, int cols,
+                                 float global_scale, hipStream_t stream) {
+  const long long nblocks = rows * (cols / kBlock);
+  const float r = (float)(1.0 / (double)global_scale);        // RN32(1/g)
+  const long long grid = (nblocks + QUANT_THREADS - 1) / QUANT_THREADS;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(nvfp4_quant_rows_kernel, dim3((unsigned)grid), dim3(QUANT_THREADS), 0, stream, x, codes, scales,
+                     nblocks, r);
+  return hipGetLastError();
+}
 
 size_t prep_workspace_bytes(int H, int L) {
   return (size_t)H * kHeadDim * (size_t)mean_chunks(L) * MEAN_SLOTS * sizeof(double);

@@ -33,6 +33,7 @@ import numpy as np
 
 D = 128
 TID_Q, TID_K, TID_V, TID_OFFSET, TID_OUTLIER, TID_DOUT = 0, 1, 2, 3, 4, 5
+TID_LIN_X, TID_LIN_W, TID_LIN_OUTLIER = 6, 7, 8
 N_OUTLIER_CHANNELS = 3          # round(0.02 * 128)
 OUTLIER_GAIN = np.float32(20.0)
 
@@ -208,3 +209,54 @@ def sample_rows(L, n_random, seed=12345, tiles=(64, 128, 256)):
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, L])))
     rand = rng.choice(L, size=min(n_random, L), replace=False)
     return np.array(sorted(fixed.union(int(r) for r in rand)), dtype=np.int64)
+
+
+# Operands of a linear layer of the same transformer (section "NVFP4 QAD":
+# every attention and feed-forward linear takes 4-bit weights and
+# activations).  The hidden size is the head configuration above (40 x 128 =
+# 5120).  Activations X [M, K]: N(0,1) values with 2% of the K channels
+# (chosen per seed) scaled x20, the outlier channels of a transformer's hidden
+# state; weights W [N, K]: N(0, 1/K).  Rows are drawn in chunks of LIN_CHUNK
+# rows, chunk c from rng (seed, tensor_id, c), so any row can be regenerated
+# alone; float32 -> BF16 round to nearest even as above.
+LIN_CHUNK = 4096
+LIN_OUTLIER_FRAC = 0.02
+
+
+def linear_outlier_channels(K, seed):
+    n = max(1, int(round(LIN_OUTLIER_FRAC * K)))
+    return np.sort(_rng(seed, TID_LIN_OUTLIER, 0).choice(K, n, replace=False))
+
+
+def _linear_chunk(kind, rows, K, seed, c):
+    n = min(LIN_CHUNK, rows - c * LIN_CHUNK)
+    if kind == "x":
+        x = _rng(seed, TID_LIN_X, c).standard_normal((n, K), dtype=np.float32)
+        x[:, linear_outlier_channels(K, seed)] *= OUTLIER_GAIN
+    else:
+        x = _rng(seed, TID_LIN_W, c).standard_normal((n, K), dtype=np.float32)
+        x *= np.float32(1.0 / math.sqrt(K))
+    return f32_to_bf16_bits(x)
+
+
+def linear_operand(kind, rows, K, seed, row_ids=None):
+    """BF16 bits of X (kind "x", [rows, K]) or W (kind "w", [rows, K]); with
+    ``row_ids`` only those rows (regenerating just their chunks)."""
+    if kind not in ("x", "w"):
+        raise ValueError(kind)
+    if row_ids is not None:
+        row_ids = np.asarray(row_ids, dtype=np.int64)
+        out = np.empty((len(row_ids), K), dtype=np.uint16)
+        for c in np.unique(row_ids // LIN_CHUNK):
+            sel = np.nonzero(row_ids // LIN_CHUNK == c)[0]
+            out[sel] = _linear_chunk(kind, rows, K, seed, int(c))[row_ids[sel] - c * LIN_CHUNK]
+        return out
+    out = np.empty((rows, K), dtype=np.uint16)
+    nchunks = (rows + LIN_CHUNK - 1) // LIN_CHUNK
+
+    def fill(c):
+        out[c * LIN_CHUNK:(c + 1) * LIN_CHUNK] = _linear_chunk(kind, rows, K, seed, c)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(nchunks)))
+    return out

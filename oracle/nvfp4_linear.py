@@ -8,7 +8,9 @@ the one of section "FP4 attention" (E2M1 values, E4M3 scale per 16).
 
 Readings (the pages give no numerics; listed in the design doc):
   * a tensor has one float32 global scale g > 0 besides its block scales: the
-    quantizer sees x' = RN32(x / g), quantizes x' by P5-P7 of oracle.nvfp4
+    quantizer sees x' = RN32(x * r) with r = RN32(1 / g) (one multiply per
+    value; equal to RN32(x / g) when g is a power of two), quantizes x' by
+    P5-P7 of oracle.nvfp4
     (blocks of 16 consecutive values along each row), and a code e with
     block scale s stands for e * s * g.  With g = 1 this is exactly the Q/K
     quantizer without rotation.  Values beyond 6 * 448 * g saturate: g sets
@@ -30,9 +32,15 @@ def quantize(x, global_scale=1.0):
     """x: float values exactly representable in BF16, [rows, K] with K a
     multiple of 16.  Returns (codes [rows, K/2] u8, scales [rows, K/16] u8)."""
     x = np.asarray(x, dtype=np.float64)
-    g = np.float32(global_scale)
-    xs = (x / np.float64(g)).astype(np.float32)          # RN32(x / g): one IEEE division, double rounding innocuous
+    r = reciprocal_f32(global_scale)
+    xs = (x * np.float64(r)).astype(np.float32)          # RN32(x * r): double rounding innocuous (53 >= 2*24+2)
     return _quantize_rows(xs, rotate=False)
+
+
+def reciprocal_f32(global_scale):
+    """r = RN32(1 / g) for a float32 g (fp64 quotient rounded to float32, an
+    innocuous double rounding)."""
+    return np.float32(1.0 / np.float64(np.float32(global_scale)))
 
 
 def dequantize(codes, scales, global_scale=1.0):
@@ -49,9 +57,11 @@ def linear(x_codes, x_scales, x_global, w_codes, w_scales, w_global):
 def linear_bound(x_codes, x_scales, x_global, w_codes, w_scales, w_global, u=2.0 ** -8):
     """Elementwise error bound of a BF16-MFMA computation of ``linear`` (test
     tolerance): products of the exact BF16 operands are exact, their fp32 sum
-    over K adds sqrt(K) 2^-24 sum |terms|, the output is rounded to BF16 (u)."""
+    over K adds sqrt(K) 2^-24 sum |terms|, the product of the two global
+    scales and its application to the sum are fp32 roundings (2^-24 each), the
+    output is rounded to BF16 (u)."""
     xh = dequantize(x_codes, x_scales, x_global)
     wh = dequantize(w_codes, w_scales, w_global)
     K = xh.shape[1]
     y = xh @ wh.T
-    return np.sqrt(K) * 2.0 ** -24 * (np.abs(xh) @ np.abs(wh).T) + u * np.abs(y)
+    return np.sqrt(K) * 2.0 ** -24 * (np.abs(xh) @ np.abs(wh).T) + (u + 2.0 ** -23) * np.abs(y)

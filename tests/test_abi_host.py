@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.lsd_abi_version() == 2
+    assert lib.lsd_abi_version() == 3
     for st in range(9):
         assert lib.lsd_status_str(st).decode()
     assert lib.lsd_status_str(99).decode() == "unknown status"
@@ -155,3 +155,38 @@ def test_bwd_fp4qk_argument_errors(lib):
     assert f(*ok, ws, need, 2, 16, 128, float("nan"), 3, N) == 7
     assert f(*ok, ws, need - 1, 2, 16, 128, 0.1, 3, N) == 5
     assert f(*ok, ctypes.c_void_p(0x200010), need, 2, 16, 128, 0.1, 3, N) == 5
+
+
+
+def test_nvfp4_quantize_argument_errors(lib):
+    f = lib.nvfp4_quantize
+    assert f(A, A, A, 0, 32, 1.0, N) == 2                               # rows
+    assert f(A, A, A, 4, 8, 1.0, N) == 2                                # cols < 16
+    assert f(A, A, A, 4, 40, 1.0, N) == 2                               # cols not a multiple of 16
+    assert f(A, A, A, 1 << 40, 16, 1.0, N) == 2                         # too many blocks for the grid
+    assert f(N, A, A, 4, 32, 1.0, N) == 1
+    assert f(A, A, N, 4, 32, 1.0, N) == 1
+    assert f(B, A, A, 4, 32, 1.0, N) == 4                               # x misaligned
+    assert f(A, B, A, 4, 32, 1.0, N) == 4                               # codes misaligned
+    assert f(A, A, A, 4, 32, 0.0, N) == 7
+    assert f(A, A, A, 4, 32, -2.0, N) == 7
+    assert f(A, A, A, 4, 32, float("inf"), N) == 7
+    assert f(A, A, A, 4, 32, 1e-45, N) == 7                             # 1/g overflows float32
+
+
+def test_nvfp4_linear_argument_errors(lib):
+    f = lib.nvfp4_linear
+    assert f(A, A, 1.0, A, A, 1.0, A, 0, 8, 64, N) == 2                 # M
+    assert f(A, A, 1.0, A, A, 1.0, A, 8, 0, 64, N) == 2                 # N
+    assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, 8, N) == 2                  # K < 16
+    assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, 72, N) == 2                 # K not a multiple of 16
+    assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, (1 << 20) + 16, N) == 2     # K too large
+    for i in (0, 1, 3, 4, 6):
+        args = [A, A, 1.0, A, A, 1.0, A]
+        args[i] = N
+        assert f(*args, 8, 8, 64, N) == 1, i
+    assert f(B, A, 1.0, A, A, 1.0, A, 8, 8, 64, N) == 4                 # x codes misaligned
+    assert f(A, A, 1.0, B, A, 1.0, A, 8, 8, 64, N) == 4
+    assert f(A, A, 1.0, A, A, 1.0, ctypes.c_void_p(0x100004), 8, 8, 64, N) == 4    # y needs 8 bytes
+    assert f(A, A, 0.0, A, A, 1.0, A, 8, 8, 64, N) == 7
+    assert f(A, A, 1.0, A, A, float("nan"), A, 8, 8, 64, N) == 7

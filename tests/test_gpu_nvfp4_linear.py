@@ -1,0 +1,175 @@
+"""GPU parity of the NVFP4 W4A4 linear layer (nvfp4_quantize, nvfp4_linear)
+against the fp64 oracle (oracle.nvfp4_linear).
+
+The quantizer's codes and scales are compared bit for bit.  The product is
+compared element by element within twice the error bound of the kernel's
+arithmetic (exact BF16 operands, fp32 sums, fp32 scaling, BF16 output);
+the oracle quantizes the same BF16 inputs itself, so no GPU value is an
+oracle input.  Small and ragged shapes (M, N not multiples of the 256 x 256
+output tile, K not a multiple of the 64-value stage, N not a multiple of 4)
+are compared in full; the full-size workload (109,000 tokens x 5120 -> 5120,
+one attention projection at the 40 x 128 hidden size) on sampled token rows,
+with every weight code checked.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from long_sequence_dense_amd import inputs
+from oracle import nvfp4_linear as ref
+
+pytestmark = pytest.mark.gpu
+
+E4M3_MAX = 448.0
+E2M1_MAX = 6.0
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    from long_sequence_dense_amd import binding
+    binding.load_library()
+    return t
+
+
+def bf16_dev(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits.view(np.int16))).cuda().view(torch.bfloat16)
+
+
+def calibrated(bits):
+    """Static global scale from a calibration pass over the tensor itself:
+    its largest magnitude maps to the largest code, 6 * 448 (a float32
+    quotient, as a host-side calibration would compute it)."""
+    amax = np.float32(np.max(np.abs(inputs.bf16_bits_to_f32(bits))))
+    return float(amax / np.float32(E2M1_MAX * E4M3_MAX))
+
+
+def gpu_quantize(torch, bits, g):
+    from long_sequence_dense_amd import binding
+    x = bf16_dev(torch, bits)
+    rows, cols = bits.shape
+    codes = torch.full((rows, cols // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows, cols // 16), 0xA5, dtype=torch.uint8, device="cuda")
+    binding.nvfp4_quantize(x, g, codes, scales)
+    torch.cuda.synchronize()
+    return codes, scales
+
+
+def check_codes(tag, got_c, got_s, bits, g):
+    want_c, want_s = ref.quantize(inputs.bf16_bits_to_f32(bits), g)
+    gc, gs = got_c.cpu().numpy(), got_s.cpu().numpy()
+    nc, ns = int(np.sum(gc != want_c)), int(np.sum(gs != want_s))
+    say("  %-28s codes %d/%d differ, scales %d/%d differ" % (tag, nc, gc.size, ns, gs.size))
+    assert nc == 0 and ns == 0
+    return want_c, want_s
+
+
+QUANT_CASES = [
+    # rows, cols, seed, scale choice
+    (1, 16, 1, "one"),
+    (37, 48, 2, "calibrated"),
+    (300, 5120, 3, "calibrated"),
+    (129, 160, 4, "pow2"),            # g = 2^-3: codes as for g = 1 with the scales shifted
+    (64, 256, 5, "clip"),             # g far below calibration: saturation at 6 * 448
+    (1000, 64, 6, "odd"),             # an arbitrary float32 g
+]
+
+
+@pytest.mark.parametrize("rows,cols,seed,gsel", QUANT_CASES)
+def test_quantize_bit_exact(torch, rows, cols, seed, gsel):
+    bits = inputs.linear_operand("x", rows, cols, seed)
+    g = {"one": 1.0, "calibrated": calibrated(bits), "pow2": 0.125, "clip": calibrated(bits) / 50.0,
+         "odd": float(np.float32(0.0123456))}[gsel]
+    say("case quantize rows=%d cols=%d seed=%d g=%s (%r)" % (rows, cols, seed, gsel, g))
+    c, s = gpu_quantize(torch, bits, g)
+    check_codes("x %dx%d" % (rows, cols), c, s, bits, g)
+
+
+def compare(tag, got, want, bound):
+    err = np.abs(got - want)
+    ratio = float(np.max(err / (2.0 * bound + 2.0 ** -120)))
+    say("  %-28s max-abs %.3e  max|ref| %.3e  max err/(2 bound) %.3f"
+        % (tag, float(err.max()), float(np.abs(want).max()), ratio))
+    assert np.all(np.isfinite(got))
+    assert ratio <= 1.0
+
+
+def to_f64(torch, y):
+    return inputs.bf16_bits_to_f32(y.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+
+
+LINEAR_CASES = [
+    # M, N, K
+    (1, 1, 16),
+    (33, 17, 48),                     # everything ragged, N odd (scalar stores)
+    (300, 260, 320),                  # 2 x 2 tiles, ragged M and N, K = 5 stages
+    (512, 512, 1024),                 # whole tiles
+    (257, 301, 80),                   # ragged K stage (80 = 64 + 16), N % 4 = 1
+    (700, 1030, 5120),                # the hidden size as K
+]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_CASES)
+def test_linear_small_full(torch, M, N, K):
+    from long_sequence_dense_amd import binding
+    say("case linear M=%d N=%d K=%d" % (M, N, K))
+    xb = inputs.linear_operand("x", M, K, 20 + M)
+    wb = inputs.linear_operand("w", N, K, 30 + N)
+    gx, gw = calibrated(xb), calibrated(wb)
+    xc, xs = gpu_quantize(torch, xb, gx)
+    wc, ws = gpu_quantize(torch, wb, gw)
+    rxc, rxs = check_codes("x", xc, xs, xb, gx)
+    rwc, rws = check_codes("w", wc, ws, wb, gw)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    binding.nvfp4_linear(xc, xs, gx, wc, ws, gw, y)
+    torch.cuda.synchronize()
+    want = ref.linear(rxc, rxs, gx, rwc, rws, gw)
+    bound = ref.linear_bound(rxc, rxs, gx, rwc, rws, gw)
+    compare("y %dx%dx%d" % (M, N, K), to_f64(torch, y), want, bound)
+
+
+def test_linear_deterministic(torch):
+    from long_sequence_dense_amd import binding
+    M, N, K = 600, 520, 640
+    say("case linear deterministic M=%d N=%d K=%d" % (M, N, K))
+    xc, xs = gpu_quantize(torch, inputs.linear_operand("x", M, K, 41), 0.01)
+    wc, ws = gpu_quantize(torch, inputs.linear_operand("w", N, K, 42), 0.001)
+    a = binding.nvfp4_linear(xc, xs, 0.01, wc, ws, 0.001)
+    b = binding.nvfp4_linear(xc, xs, 0.01, wc, ws, 0.001)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+FULL_M, FULL_N, FULL_K = 109000, 5120, 5120
+
+
+def test_linear_full_size(torch):
+    """Full-size projection as the benchmark runs it: all weight codes bit
+    exact, sampled token rows' codes bit exact and their outputs within the
+    bound."""
+    from long_sequence_dense_amd import binding
+    say("case linear full M=%d N=%d K=%d (generate)" % (FULL_M, FULL_N, FULL_K))
+    xb = inputs.linear_operand("x", FULL_M, FULL_K, 7)
+    wb = inputs.linear_operand("w", FULL_N, FULL_K, 8)
+    gx, gw = calibrated(xb), calibrated(wb)
+    xc, xs = gpu_quantize(torch, xb, gx)
+    del xb
+    wc, ws = gpu_quantize(torch, wb, gw)
+    rwc, rws = check_codes("w all rows", wc, ws, wb, gw)
+    y = binding.nvfp4_linear(xc, xs, gx, wc, ws, gw)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(FULL_M, 48, seed=77, tiles=(256,))
+    xr = inputs.linear_operand("x", FULL_M, FULL_K, 7, row_ids=rows)
+    idx = torch.from_numpy(rows).cuda()
+    rxc, rxs = check_codes("x sampled rows", xc.index_select(0, idx), xs.index_select(0, idx), xr, gx)
+    want = ref.linear(rxc, rxs, gx, rwc, rws, gw)
+    bound = ref.linear_bound(rxc, rxs, gx, rwc, rws, gw)
+    compare("y sampled rows", to_f64(torch, y.index_select(0, idx)), want, bound)

@@ -79,3 +79,17 @@ def test_toy_heads_structure():
     # spread far more than those of Q (outlier channels aside)
     assert np.std(k.mean(axis=1)) > 2 * np.std(np.median(q, axis=1))
     assert abs(np.std(v) - 1.0) < 0.1
+
+
+def test_linear_operands_rows_regenerate():
+    # any row set regenerates alone (chunked seeding), X carries its outlier
+    # channels, W has variance about 1/K
+    x = inputs.linear_operand("x", 5000, 64, 3)
+    rows = [0, 4095, 4096, 4999]
+    assert np.array_equal(inputs.linear_operand("x", 5000, 64, 3, row_ids=rows), x[rows])
+    xf = inputs.bf16_bits_to_f32(x)
+    ch = inputs.linear_outlier_channels(64, 3)
+    assert len(ch) == 1
+    assert 15 < np.std(xf[:, ch]) < 25 and 0.9 < np.std(np.delete(xf, ch, axis=1)) < 1.1
+    w = inputs.bf16_bits_to_f32(inputs.linear_operand("w", 256, 1024, 4))
+    assert abs(np.var(w) * 1024 - 1) < 0.05
