@@ -33,10 +33,14 @@ constexpr int GM = 256;                 // tokens (rows of Y) per workgroup
 constexpr int GN = 256;                 // features (columns of Y) per workgroup
 constexpr int GK = 64;                  // K per LDS stage
 constexpr int GT = 512;                 // threads per workgroup
-constexpr int GS = GK + 8;              // LDS row stride (bf16)
+constexpr int GS = GK + 8;              // LDS row stride (fp16 values)
 constexpr int NB = GK / kBlock;         // 16-value blocks per row per stage
 constexpr int SB = (GN * NB) / GT;      // blocks of one operand staged per thread per stage
 constexpr int kOutside = 0x7FFFFFF0;    // a byte offset past every buffer range (loads return 0)
+static_assert(GM == GN && SB == 2, "staging assumes square tiles and two blocks per thread");
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 struct GemmParams {
   const uint8_t* xc;
@@ -46,20 +50,22 @@ struct GemmParams {
   uint16_t* y;
   int M, N, K;
   int tiles_n, tiles;
-  float gscale;                         // g_x * g_w
+  float gscale;                         // RN32(g_x * g_w)
 };
 
-struct GemmSmem {
-  uint16_t w[2][GN * GS];
-  uint16_t x[2][GM * GS];
-};
+// Two LDS buffers per operand, as separate objects so that the compiler
+// knows the stores into one never alias the operand reads from the other.
+__shared__ __attribute__((aligned(16))) uint16_t lw0[GN * GS];
+__shared__ __attribute__((aligned(16))) uint16_t lw1[GN * GS];
+__shared__ __attribute__((aligned(16))) uint16_t lx0[GM * GS];
+__shared__ __attribute__((aligned(16))) uint16_t lx1[GM * GS];
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long long bytes) {
   const int n = bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-// Codes and scales of one operand's stage, this thread's share: block id
+// Codes and scales of one operand's stage, this thread's share: block
 // b = tid + GT * i covers row b / NB, values 16 * (b % NB) .. +15 of the stage.
 struct Stage {
   u32x2 c[SB];
@@ -72,7 +78,8 @@ __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rc, __amdgpu_b
   for (int i = 0; i < SB; ++i) {
     const int b = tid + GT * i;
     const int row = b / NB, kb = b % NB;
-    // blocks past K (a ragged last stage) read beyond the buffer range: zeros
+    // blocks past K (a ragged last stage, or a stage past the end) read
+    // beyond the buffer range: zeros
     const bool in = k0 + kBlock * kb < K;
     const int oc = in ? row * (K / 2) + k0 / 2 + 8 * kb : kOutside;
     const int os = in ? row * (K / kBlock) + k0 / kBlock + kb : kOutside;
@@ -81,23 +88,58 @@ __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rc, __amdgpu_b
   }
 }
 
-__device__ __forceinline__ void store_stage(uint16_t* tile, int tid, const Stage& st) {
+// Exact dequantization of block i of a stage into an LDS tile: an E2M1 value
+// times an E4M3 scale has at most 6 significant bits and lies in [2^-10,
+// 2688] when nonzero, so it is exact in FP16 (normal range) as well as BF16.
+// The packed FP16 multiply takes two values per instruction.
+__device__ __forceinline__ void put_block(uint16_t* tile, int tid, int i, const Stage& st) {
+  const int b = tid + GT * i;
+  const int row = b / NB, kb = b % NB;
+  // E4M3 scale code c (sign clear) to FP16: the bits c << 7 read as FP16
+  // carry the exponent and mantissa fields (biases 15 vs 7, codes with a zero
+  // exponent land on FP16 subnormals of the same form), times 2^8 exact.
+  const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)((st.s[i] & 0x7Fu) << 7)) * (_Float16)256.0f;
+  const f16x2 s2 = {sh, sh};
+  u32x4 lo, hi;
+  lo[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][0], 1.0f, 0) * s2);
+  lo[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][0], 1.0f, 1) * s2);
+  lo[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][0], 1.0f, 2) * s2);
+  lo[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][0], 1.0f, 3) * s2);
+  hi[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][1], 1.0f, 0) * s2);
+  hi[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][1], 1.0f, 1) * s2);
+  hi[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][1], 1.0f, 2) * s2);
+  hi[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][1], 1.0f, 3) * s2);
+  *(u32x4*)(tile + row * GS + kBlock * kb) = lo;
+  *(u32x4*)(tile + row * GS + kBlock * kb + 8) = hi;
+}
+
+__device__ __forceinline__ f16x8 operand(const uint16_t* tile, int lane_off, int row0, int ks) {
+  return __builtin_bit_cast(f16x8, *(const u16x8*)(tile + row0 * GS + lane_off + 16 * ks));
+}
+
+// One K stage: multiply the tiles in (wt, xt) while the codes in (dw, dx),
+// the next stage, are dequantized into (wd, xd), one block per 16-wide step.
+__device__ __forceinline__ void stage_step(const uint16_t* wt, const uint16_t* xt, uint16_t* wd, uint16_t* xd,
+                                           const Stage& dw, const Stage& dx, f32x16 (&acc)[4][2], int lane_off,
+                                           int wn, int wm, int tid) {
 #pragma unroll
-  for (int i = 0; i < SB; ++i) {
-    const int b = tid + GT * i;
-    const int row = b / NB, kb = b % NB;
-    const float sc = e4m3_to_f32(st.s[i] & 0xFF);
-    *(u16x8*)(tile + row * GS + 16 * kb) = dequant8(st.c[i][0], sc);
-    *(u16x8*)(tile + row * GS + 16 * kb + 8) = dequant8(st.c[i][1], sc);
+  for (int ks = 0; ks < GK / 16; ++ks) {
+    f16x8 a[4], b[2];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) a[nb] = operand(wt, lane_off, 128 * wn + 32 * nb, ks);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) b[mb] = operand(xt, lane_off, 64 * wm + 32 * mb, ks);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+    if (ks < 2) put_block(wd, tid, ks, dw);
+    else put_block(xd, tid, ks - 2, dx);
   }
 }
 
-__device__ __forceinline__ bf16x8 operand(const uint16_t* tile, int lane_off, int row0, int ks) {
-  return __builtin_bit_cast(bf16x8, *(const u16x8*)(tile + row0 * GS + lane_off + 16 * ks));
-}
-
 __global__ __launch_bounds__(GT, 1) void nvfp4_gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) GemmSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -126,44 +168,33 @@ __global__ __launch_bounds__(GT, 1) void nvfp4_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = (f32x16)0.0f;
 
+  // Register stages: stage s lives in set s % 2 from the top of step s - 2
+  // (when it is loaded) to step s - 1 (when it is dequantized into LDS
+  // buffer s % 2, which step s multiplies).
   const int nst = (K + GK - 1) / GK;
-  {
-    Stage sw, sx;
-    load_stage(rwc, rws, K, 0, tid, sw);
-    load_stage(rxc, rxs, K, 0, tid, sx);
-    store_stage(sm.w[0], tid, sw);
-    store_stage(sm.x[0], tid, sx);
+  Stage w0, x0, w1, x1;
+  load_stage(rwc, rws, K, 0, tid, w0);
+  load_stage(rxc, rxs, K, 0, tid, x0);
+  load_stage(rwc, rws, K, GK, tid, w1);
+  load_stage(rxc, rxs, K, GK, tid, x1);
+#pragma unroll
+  for (int i = 0; i < SB; ++i) {
+    put_block(lw0, tid, i, w0);
+    put_block(lx0, tid, i, x0);
   }
   __syncthreads();
 
-  for (int s = 0; s < nst; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nst;
-    Stage sw, sx;
-    if (more) {
-      load_stage(rwc, rws, K, (s + 1) * GK, tid, sw);
-      load_stage(rxc, rxs, K, (s + 1) * GK, tid, sx);
-    }
-    const uint16_t* wt = sm.w[buf];
-    const uint16_t* xt = sm.x[buf];
-#pragma unroll
-    for (int ks = 0; ks < GK / 16; ++ks) {
-      bf16x8 a[4], b[2];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) a[nb] = operand(wt, lane_off, 128 * wn + 32 * nb, ks);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) b[mb] = operand(xt, lane_off, 64 * wm + 32 * mb, ks);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
-    }
-    if (more) {
-      store_stage(sm.w[buf ^ 1], tid, sw);
-      store_stage(sm.x[buf ^ 1], tid, sx);
-    }
+  for (int s = 0; s < nst; s += 2) {
+    load_stage(rwc, rws, K, (s + 2) * GK, tid, w0);
+    load_stage(rxc, rxs, K, (s + 2) * GK, tid, x0);
+    stage_step(lw0, lx0, lw1, lx1, w1, x1, acc, lane_off, wn, wm, tid);
     __syncthreads();
+    if (s + 1 < nst) {
+      load_stage(rwc, rws, K, (s + 3) * GK, tid, w1);
+      load_stage(rxc, rxs, K, (s + 3) * GK, tid, x1);
+      stage_step(lw1, lx1, lw0, lx0, w0, x0, acc, lane_off, wn, wm, tid);
+      __syncthreads();
+    }
   }
 
   // Y^T block (nb, mb): lane holds token m0 + 64 wm + 32 mb + l32 and, per
