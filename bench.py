@@ -132,6 +132,63 @@ def cpu_baseline(H, L, d):
     }
 
 
+LIN_M, LIN_N, LIN_K = 109000, 5120, 5120
+
+
+def linear_operands(torch, dev):
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    x = torch.randn((LIN_M, LIN_K), dtype=torch.float32, device=dev, generator=gen)
+    ch = torch.randperm(LIN_K, generator=torch.Generator().manual_seed(6))[:round(0.02 * LIN_K)].to(dev)
+    x[:, ch] *= 20.0
+    x = x.to(torch.bfloat16)
+    w = (torch.randn((LIN_N, LIN_K), dtype=torch.float32, device=dev, generator=gen) * LIN_K ** -0.5).to(torch.bfloat16)
+    gx = float(x.float().abs().max().item()) / (6.0 * 448.0)
+    gw = float(w.float().abs().max().item()) / (6.0 * 448.0)
+    return x, w, gx, gw
+
+
+def time_calls(torch, stream, fn, n=3):
+    times = []
+    for i in range(n + 1):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        if i:
+            times.append(a.elapsed_time(b))
+    return sum(times) / len(times)
+
+
+def linear_path(torch, binding, stream, dev):
+    x, w, gx, gw = linear_operands(torch, dev)
+    M, N, K = LIN_M, LIN_N, LIN_K
+    T = binding.NVFP4_TILED                      # the product's own load order
+    xc, xs = binding.nvfp4_quantize(x, gx, layout=T, stream=stream)
+    wc, ws = binding.nvfp4_quantize(w, gw, layout=T, stream=stream)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t_q = time_calls(torch, stream, lambda: binding.nvfp4_quantize(x, gx, xc, xs, layout=T, stream=stream))
+    t_l = time_calls(torch, stream, lambda: binding.nvfp4_linear(xc, xs, gx, wc, ws, gw, y, stream=stream,
+                                                                 layout=T, M=M, N=N, K=K))
+    assert not torch.isnan(y).any().item()
+    qbytes = M * K * 2 + M * K // 2 + M * K // 16    # (the tiled padding of the last tile not counted)
+    qg = qbytes / (t_q * 1e-3) / 1e9
+    lf = 2.0 * M * N * K
+    lt = lf / (t_l * 1e-3) / 1e12
+    wl = "M=%d tokens, N=%d, K=%d" % (M, N, K)
+    return {
+        "nvfp4_quantize": {"ms": round(t_q, 4), "GB/s": round(qg, 1), "algorithmic_bytes": qbytes,
+                           "frac_of_peak": round(qg / PEAK_HBM_GBS, 4), "workload": "X of " + wl + ", tiled code layout",
+                           "in_value": False},
+        "nvfp4_linear": {"ms": round(t_l, 3), "TFLOP/s": round(lt, 1), "algorithmic_flop": lf,
+                         "frac_of_peak": round(lt / PEAK_BF16_TFLOPS, 4),
+                         "mfma_precision": "fp16 (exact dequantization of NVFP4 X and W)",
+                         "workload": wl + ", tiled code layout", "in_value": False},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +199,8 @@ def main():
                     help="bf16: time only attn_fwd_bf16 (for profiling runs)")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the extra (not in value) timing of attn_bwd_bf16")
+    ap.add_argument("--no-linear", action="store_true",
+                    help="skip the extra (not in value) timing of the NVFP4 linear layer")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for hardware-counter runs: one %d-byte torch copy (counter calibration), "
                          "then one launch of each kernel on the benchmark workload; no timing" % COPY_PROBE_BYTES)
@@ -205,6 +264,12 @@ def main():
         b.copy_(a)                                   # the calibration copy
         torch.cuda.synchronize()
         step(False)
+        torch.cuda.synchronize()
+        x, w, gx, gw = linear_operands(torch, dev)
+        T = binding.NVFP4_TILED
+        xc, xs = binding.nvfp4_quantize(x, gx, layout=T, stream=stream)
+        wc, ws_ = binding.nvfp4_quantize(w, gw, layout=T, stream=stream)
+        binding.nvfp4_linear(xc, xs, gx, wc, ws_, gw, stream=stream, layout=T, M=LIN_M, N=LIN_N, K=LIN_K)
         torch.cuda.synchronize()
         log("pmc probe done")
         return
@@ -274,6 +339,15 @@ def main():
                                                      "compute 7 (S and dP again for dQ)",
                                   "in_value": False}
         del grads, dout, bws
+    if args.only != "bf16" and not args.no_linear:
+        # Extra path, outside the step and its value: one NVFP4 W4A4 linear of
+        # the same transformer at the 40 x 128 hidden size, over the clip's
+        # tokens (X [109000, 5120], W [5120, 5120]); seeded device draws, X
+        # N(0,1) with 2% of its channels x20, W N(0, 1/5120); static global
+        # scales from the tensors' maxima.  1 warm-up + 3 timed calls each.
+        log("timing nvfp4_quantize + nvfp4_linear (3 calls each) ...")
+        r = linear_path(torch, binding, stream, dev)
+        paths.update(r)
     traffic = stored_traffic()
     res = {
         "metric": METRIC,

@@ -14,7 +14,8 @@
  *   attn_bwd_fp4qk  training-time gradients of attn_fwd_fp4qk (straight-
  *                   through quantizer), with respect to the original Q, K, V.
  *   nvfp4_quantize  NVFP4 quantization (per-tensor global scale) of the rows
- *                   of a linear layer's activation or weight matrix.
+ *                   of a linear layer's activation or weight matrix, row-major
+ *                   or in the product's tiled load order.
  *   nvfp4_linear    the W4A4 linear layer Y = X W^T from two such operands.
  *
  * The method is the one of "Pika H3 Flex in FastVideo: 7x Faster, and Near
@@ -62,7 +63,7 @@ enum lsd_status {
   LSD_ERR_WORKSPACE = 5,      /* workspace missing, misaligned or too small   */
   LSD_ERR_LAUNCH = 6,         /* the HIP runtime rejected a kernel launch     */
   LSD_ERR_SCALE = 7,          /* a scale argument is not finite and positive  */
-  LSD_ERR_FLAGS = 8           /* unknown bits in a flags argument             */
+  LSD_ERR_FLAGS = 8           /* unknown bits in a flags or layout argument    */
 };
 
 /* Version of this ABI (the value of LSD_ABI_VERSION the library was built with). */
@@ -235,18 +236,40 @@ int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales,
                    void* workspace, size_t workspace_bytes,
                    int H, int L, int d, float softmax_scale, int flags, void* stream);
 
+/* Code layouts of nvfp4_quantize / nvfp4_linear operands. */
+enum lsd_nvfp4_layout {
+  LSD_NVFP4_ROWS = 0,   /* codes [rows, cols / 2], scales [rows, cols / 16], row-major     */
+  LSD_NVFP4_TILED = 1   /* the product's load order: see nvfp4_codes_bytes                 */
+};
+
+/*
+ * Bytes of the code and scale buffers of a [rows, cols] operand in a layout
+ * (0 on bad arguments: rows < 1 or > 2^40, cols < 16 or not a multiple of 16,
+ * unknown layout).
+ *   LSD_NVFP4_ROWS : rows * cols / 2 and rows * cols / 16.
+ *   LSD_NVFP4_TILED: rows are grouped in tiles of 256 and each row's values in
+ *     stages of 64 (both zero-padded at the end); chunk (t, s), ordered
+ *     t-major, holds rows 256 t .. 256 t + 255, values 64 s .. 64 s + 63 of
+ *     each: 8192 code bytes (row r of the tile at 32 r, in the row-major byte
+ *     order) and 1024 scale bytes (row r at 4 r).  ceil(rows / 256) *
+ *     ceil(cols / 64) * 8192 and * 1024 bytes.  Padding holds zeros (code 0,
+ *     scale 0: value 0).
+ */
+size_t nvfp4_codes_bytes(long long rows, int cols, int layout);
+size_t nvfp4_scales_bytes(long long rows, int cols, int layout);
+
 /*
  * nvfp4_quantize - NVFP4 codes of a row-major [rows, cols] BF16 matrix (an
  * activation X or a weight W of a linear layer).
  *   x       : [rows, cols] BF16 bits, read only, 16-byte aligned.
- *   codes   : [rows, cols / 2] bytes, written; byte j of a row holds value
- *             2j in its low nibble and 2j+1 in its high nibble (E2M1: sign
- *             bit 3, magnitude index 0..7 for 0, .5, 1, 1.5, 2, 3, 4, 6).
- *             16-byte aligned.
- *   scales  : [rows, cols / 16] E4M3 codes (one per 16 consecutive values of
- *             a row), written.
- *   rows >= 1, cols >= 16 and a multiple of 16, rows * cols / 16 < 2^31 * 256
- *   (else LSD_ERR_SHAPE).
+ *   codes   : nvfp4_codes_bytes(rows, cols, layout) bytes, written, 16-byte
+ *             aligned.  Within a row, byte j holds value 2j in its low nibble
+ *             and 2j+1 in its high nibble (E2M1: sign bit 3, magnitude index
+ *             0..7 for 0, .5, 1, 1.5, 2, 3, 4, 6).
+ *   scales  : nvfp4_scales_bytes(rows, cols, layout) bytes, written: one E4M3
+ *             code per 16 consecutive values of a row.
+ *   rows >= 1, cols >= 16 and a multiple of 16, rows * cols / 16 < 2^39
+ *   (else LSD_ERR_SHAPE); layout an lsd_nvfp4_layout (else LSD_ERR_FLAGS).
  *   global_scale : g, float32, finite, > 0 and with a finite float32 1/g
  *             (else LSD_ERR_SCALE).  The quantizer sees x' = RN32(x * RN32(1/g))
  *             and quantizes each block of 16 as qk_prep_fp4 does (E4M3 scale
@@ -259,7 +282,7 @@ int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales,
  * scales from calibration) with the block format of "FP4 attention".
  */
 int nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long rows, int cols,
-                   float global_scale, void* stream);
+                   float global_scale, int layout, void* stream);
 
 /*
  * nvfp4_linear - Y = (X^ g_x) (W^ g_w)^T, the W4A4 linear layer.
@@ -267,18 +290,21 @@ int nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long
  *                       with global scale x_global_scale.
  *   w_codes, w_scales : the weight, [N, K] (one row per output feature),
  *                       quantized with global scale w_global_scale.
- *   y       : [M, N] BF16 bits, written (round to nearest even).
+ *   layout  : the layout both operands were quantized in (else
+ *             LSD_ERR_FLAGS); LSD_NVFP4_TILED is the faster one (every load
+ *             of the product reads whole cache lines).
+ *   y       : [M, N] BF16 bits, row-major, written (round to nearest even).
  *   M >= 1, N >= 1, K >= 16 and a multiple of 16, K <= 2^20 (else
  *   LSD_ERR_SHAPE); the scales must be finite and > 0 (else LSD_ERR_SCALE);
  *   code pointers 16-byte aligned, y 8-byte aligned (else LSD_ERR_ALIGN).
- * Both operands are dequantized exactly to BF16 on chip (an E2M1 value times
- * an E4M3 scale fits BF16), their products accumulate in fp32 on the matrix
+ * Both operands are dequantized exactly on chip (an E2M1 value times an E4M3
+ * scale fits FP16 and BF16), their products accumulate in fp32 on the matrix
  * cores, the fp32 sum is multiplied by RN32(g_x * g_w) and rounded to BF16.
  * No bias, no activation function.
  */
 int nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, float x_global_scale,
                  const uint8_t* w_codes, const uint8_t* w_scales, float w_global_scale,
-                 uint16_t* y, int M, int N, int K, void* stream);
+                 uint16_t* y, int M, int N, int K, int layout, void* stream);
 
 #ifdef __cplusplus
 }

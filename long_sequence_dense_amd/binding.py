@@ -22,6 +22,8 @@ STATUS = {
 }
 PREP_SMOOTH_K = 1       # lsd_prep_flags
 PREP_ROTATE = 2
+NVFP4_ROWS = 0          # lsd_nvfp4_layout
+NVFP4_TILED = 1
 
 # name -> (restype, argtypes); mirrors include/lsd_attn.h
 _P = ctypes.c_void_p
@@ -40,8 +42,10 @@ SIGNATURES = {
     "attn_bwd_bf16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _F, _P]),
     "attn_bwd_fp4qk_workspace_bytes": (_S, [_I, _I, _I]),
     "attn_bwd_fp4qk": (_I, [_P] * 12 + [_S, _I, _I, _I, _F, _I, _P]),
-    "nvfp4_quantize": (_I, [_P, _P, _P, ctypes.c_longlong, _I, _F, _P]),
-    "nvfp4_linear": (_I, [_P, _P, _F, _P, _P, _F, _P, _I, _I, _I, _P]),
+    "nvfp4_codes_bytes": (_S, [ctypes.c_longlong, _I, _I]),
+    "nvfp4_scales_bytes": (_S, [ctypes.c_longlong, _I, _I]),
+    "nvfp4_quantize": (_I, [_P, _P, _P, ctypes.c_longlong, _I, _F, _I, _P]),
+    "nvfp4_linear": (_I, [_P, _P, _F, _P, _P, _F, _P, _I, _I, _I, _I, _P]),
 }
 
 _lib = None
@@ -275,40 +279,65 @@ def attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, dout, dq=Non
     return tuple(outs)
 
 
-def nvfp4_quantize(x, global_scale=1.0, codes=None, scales=None, stream=None):
-    """NVFP4 codes [rows, cols/2] and E4M3 block scales [rows, cols/16] of a
-    [rows, cols] BF16 matrix quantized with per-tensor global scale g."""
+def nvfp4_codes_bytes(rows, cols, layout=NVFP4_ROWS):
+    return int(load_library().nvfp4_codes_bytes(int(rows), int(cols), int(layout)))
+
+
+def nvfp4_scales_bytes(rows, cols, layout=NVFP4_ROWS):
+    return int(load_library().nvfp4_scales_bytes(int(rows), int(cols), int(layout)))
+
+
+def _nvfp4_shapes(rows, cols, layout):
+    if layout == NVFP4_ROWS:
+        return (rows, cols // 2), (rows, cols // 16)
+    return (nvfp4_codes_bytes(rows, cols, layout),), (nvfp4_scales_bytes(rows, cols, layout),)
+
+
+def nvfp4_quantize(x, global_scale=1.0, codes=None, scales=None, layout=NVFP4_ROWS, stream=None):
+    """NVFP4 codes and E4M3 block scales of a [rows, cols] BF16 matrix
+    quantized with per-tensor global scale g: row-major ([rows, cols/2],
+    [rows, cols/16]) or, with layout=NVFP4_TILED, 1-D buffers in the product's
+    tiled load order."""
     import torch
     if x.dim() != 2:
         raise ValueError("x must be [rows, cols]")
     rows, cols = x.shape
     _need(x, "x", _bf16_types(), (rows, cols))
+    cshape, sshape = _nvfp4_shapes(rows, cols, layout)
     if codes is None:
-        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
-    _need(codes, "codes", (torch.uint8,), (rows, cols // 2))
-    _need(scales, "scales", (torch.uint8,), (rows, cols // 16))
+        scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
+    _need(codes, "codes", (torch.uint8,), cshape)
+    _need(scales, "scales", (torch.uint8,), sshape)
     st = load_library().nvfp4_quantize(_ptr(x), _ptr(codes), _ptr(scales), rows, cols, float(global_scale),
-                                       _stream(stream))
+                                       int(layout), _stream(stream))
     _check("nvfp4_quantize", st)
     return codes, scales
 
 
-def nvfp4_linear(x_codes, x_scales, x_global_scale, w_codes, w_scales, w_global_scale, y=None, stream=None):
+def nvfp4_linear(x_codes, x_scales, x_global_scale, w_codes, w_scales, w_global_scale, y=None, stream=None,
+                 layout=NVFP4_ROWS, M=None, N=None, K=None):
     """Y [M, N] BF16 = (X^ g_x)(W^ g_w)^T from NVFP4 operands X [M, K] and
-    W [N, K] (codes [rows, K/2], scales [rows, K/16])."""
+    W [N, K].  Row-major operands carry M, N, K in their shapes; tiled ones
+    need them passed."""
     import torch
-    M, K = x_codes.shape[0], 2 * x_codes.shape[1]
-    N = w_codes.shape[0]
-    _need(x_codes, "x_codes", (torch.uint8,), (M, K // 2))
-    _need(x_scales, "x_scales", (torch.uint8,), (M, K // 16))
-    _need(w_codes, "w_codes", (torch.uint8,), (N, K // 2))
-    _need(w_scales, "w_scales", (torch.uint8,), (N, K // 16))
+    if layout == NVFP4_ROWS:
+        M, K = x_codes.shape[0], 2 * x_codes.shape[1]
+        N = w_codes.shape[0]
+    elif M is None or N is None or K is None:
+        raise ValueError("tiled operands need M, N and K")
+    xcs, xss = _nvfp4_shapes(M, K, layout)
+    wcs, wss = _nvfp4_shapes(N, K, layout)
+    _need(x_codes, "x_codes", (torch.uint8,), xcs)
+    _need(x_scales, "x_scales", (torch.uint8,), xss)
+    _need(w_codes, "w_codes", (torch.uint8,), wcs)
+    _need(w_scales, "w_scales", (torch.uint8,), wss)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x_codes.device)
     _need(y, "y", _bf16_types(), (M, N))
     st = load_library().nvfp4_linear(_ptr(x_codes), _ptr(x_scales), float(x_global_scale), _ptr(w_codes),
-                                     _ptr(w_scales), float(w_global_scale), _ptr(y), M, N, K, _stream(stream))
+                                     _ptr(w_scales), float(w_global_scale), _ptr(y), M, N, K, int(layout),
+                                     _stream(stream))
     _check("nvfp4_linear", st)
     return y

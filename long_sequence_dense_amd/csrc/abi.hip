@@ -28,6 +28,9 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // offsets: L * d * 2 bytes must stay below 2^31.
 int check_attn_len(int L) { return L < (1 << 23) ? LSD_OK : LSD_ERR_SHAPE; }
 
+size_t nvfp4_tiles(long long rows) { return (size_t)((rows + lsd::kLinTileRows - 1) / lsd::kLinTileRows); }
+size_t nvfp4_stages(int cols) { return (size_t)((cols + lsd::kLinStage - 1) / lsd::kLinStage); }
+
 }  // namespace
 
 extern "C" {
@@ -44,7 +47,7 @@ const char* lsd_status_str(int status) {
     case LSD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case LSD_ERR_LAUNCH: return "kernel launch failed";
     case LSD_ERR_SCALE: return "scale must be finite and > 0";
-    case LSD_ERR_FLAGS: return "unknown flag bits";
+    case LSD_ERR_FLAGS: return "unknown flag bits or layout";
     default: return "unknown status";
   }
 }
@@ -162,28 +165,46 @@ int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
                                                   (hipStream_t)stream));
 }
 
+size_t nvfp4_codes_bytes(long long rows, int cols, int layout) {
+  if (rows < 1 || cols < lsd::kBlock || cols % lsd::kBlock || rows > (1LL << 40)) return 0;
+  if (layout == LSD_NVFP4_ROWS) return (size_t)rows * (size_t)(cols / 2);
+  if (layout != LSD_NVFP4_TILED) return 0;
+  return nvfp4_tiles(rows) * nvfp4_stages(cols) * (size_t)(lsd::kLinTileRows * lsd::kLinStage / 2);
+}
+
+size_t nvfp4_scales_bytes(long long rows, int cols, int layout) {
+  if (rows < 1 || cols < lsd::kBlock || cols % lsd::kBlock || rows > (1LL << 40)) return 0;
+  if (layout == LSD_NVFP4_ROWS) return (size_t)rows * (size_t)(cols / lsd::kBlock);
+  if (layout != LSD_NVFP4_TILED) return 0;
+  return nvfp4_tiles(rows) * nvfp4_stages(cols) * (size_t)(lsd::kLinTileRows * lsd::kLinStage / lsd::kBlock);
+}
+
 int nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long rows, int cols,
-                   float global_scale, void* stream) {
+                   float global_scale, int layout, void* stream) {
+  if (layout != LSD_NVFP4_ROWS && layout != LSD_NVFP4_TILED) return LSD_ERR_FLAGS;
   if (rows < 1 || cols < lsd::kBlock || cols % lsd::kBlock) return LSD_ERR_SHAPE;
-  if (rows > (LLONG_MAX / cols) || rows * (cols / lsd::kBlock) >= (1LL << 39)) return LSD_ERR_SHAPE;
+  if (rows > (1LL << 40) || rows * (cols / lsd::kBlock) >= (1LL << 39)) return LSD_ERR_SHAPE;
   if (!x || !codes || !scales) return LSD_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes)) return LSD_ERR_ALIGN;
   if (check_scale(global_scale) != LSD_OK || !std::isfinite((float)(1.0 / (double)global_scale)))
     return LSD_ERR_SCALE;
   (void)hipGetLastError();
-  return launch_status(lsd::launch_nvfp4_quantize(x, codes, scales, rows, cols, global_scale, (hipStream_t)stream));
+  return launch_status(lsd::launch_nvfp4_quantize(x, codes, scales, rows, cols, global_scale,
+                                                  layout == LSD_NVFP4_TILED, (hipStream_t)stream));
 }
 
 int nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, float x_global_scale,
                  const uint8_t* w_codes, const uint8_t* w_scales, float w_global_scale,
-                 uint16_t* y, int M, int N, int K, void* stream) {
+                 uint16_t* y, int M, int N, int K, int layout, void* stream) {
+  if (layout != LSD_NVFP4_ROWS && layout != LSD_NVFP4_TILED) return LSD_ERR_FLAGS;
   if (M < 1 || N < 1 || K < lsd::kBlock || K % lsd::kBlock || K > (1 << 20)) return LSD_ERR_SHAPE;
   if (!x_codes || !x_scales || !w_codes || !w_scales || !y) return LSD_ERR_NULL;
   if (!aligned16(x_codes) || !aligned16(w_codes) || ((uintptr_t)y & 7u)) return LSD_ERR_ALIGN;
   if (check_scale(x_global_scale) != LSD_OK || check_scale(w_global_scale) != LSD_OK) return LSD_ERR_SCALE;
   (void)hipGetLastError();
   return launch_status(lsd::launch_nvfp4_linear(x_codes, x_scales, x_global_scale, w_codes, w_scales,
-                                                w_global_scale, y, M, N, K, (hipStream_t)stream));
+                                                w_global_scale, y, M, N, K, layout == LSD_NVFP4_TILED,
+                                                (hipStream_t)stream));
 }
 
 }  // extern "C"

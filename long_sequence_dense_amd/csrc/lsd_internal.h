@@ -35,10 +35,14 @@ hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uin
                           uint8_t* kc, uint8_t* ks, float* kmean, void* ws, int H, int L,
                           bool smooth, bool rotate, hipStream_t stream);
 
-// NVFP4 W4A4 linear layer (qk_prep.hip: quantizer, nvfp4_gemm.hip: product)
+// NVFP4 W4A4 linear layer (qk_prep.hip: quantizer, nvfp4_gemm.hip: product).
+// Tiled code layout: rows in tiles of kLinTileRows, K in stages of kLinStage
+// values, one contiguous chunk of codes (and one of scales) per (tile, stage).
+constexpr int kLinTileRows = 256;
+constexpr int kLinStage = 64;
 hipError_t launch_nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long rows, int cols,
-                                 float global_scale, hipStream_t stream);
+                                 float global_scale, bool tiled, hipStream_t stream);
 hipError_t launch_nvfp4_linear(const uint8_t* xc, const uint8_t* xs, float gx, const uint8_t* wc, const uint8_t* ws,
-                               float gw, uint16_t* y, int M, int N, int K, hipStream_t stream);
+                               float gw, uint16_t* y, int M, int N, int K, bool tiled, hipStream_t stream);
 
 }  // namespace lsd

@@ -6,23 +6,27 @@
 // section "FP4 attention": E2M1 values, an E4M3 scale per 16 consecutive
 // values along K), plus one fp32 global scale per tensor.
 //
-// gfx950's scaled MFMA takes power-of-two (E8M0) scales per 32 values; an
-// E4M3 scale per 16 values cannot be folded into it.  E2M1 x E4M3 products
-// have at most 6 significant bits, so they are exact in BF16: both operands
-// are dequantized exactly while they are staged into LDS and multiplied on the
-// 32x32x16 BF16 MFMA with fp32 accumulation; the product of the two global
-// scales is applied to the fp32 result, which is rounded to BF16.
+// gfx950's scaled MFMA takes power-of-two (E8M0) scales per 32 values, and
+// its scaled FP4 conversions apply only the power of two of their scale; an
+// E4M3 scale per 16 values cannot be folded into either.  E2M1 x E4M3
+// products have at most 6 significant bits and lie in [2^-10, 2688], so they
+// are exact in FP16 (and BF16): both operands are dequantized exactly while
+// they are staged into LDS (FP4 -> packed FP16 conversion, packed FP16
+// multiply by the block scale) and multiplied on the 32x32x16 FP16 MFMA with
+// fp32 accumulation; the product of the two global scales is applied to the
+// fp32 result, which is rounded to BF16.
 //
 // Tiling: a workgroup computes a 256 (tokens m) x 256 (features n) tile of Y
 // as Y^T blocks (W rows are the A operand, X rows the B operand, so that a
 // lane's accumulator holds four consecutive features of one token); eight
 // waves (two per SIMD) of 128 (n) x 64 (m), i.e. 4 x 2 blocks of 32 x 32.  K
 // advances 64 at a time through double-buffered LDS tiles (row stride 144 B:
-// the operand reads are free of bank conflicts); the codes of the next stage
-// are loaded into registers while the current one is multiplied.  Workgroups
-// are numbered so that consecutive ones share the X rows and each XCD (own L2)
-// takes a contiguous range.  Rows past M or N and blocks past K load as zeros;
-// rows past M or N are not stored.
+// the operand reads are free of bank conflicts); the codes of stage s + 1,
+// loaded into registers one step earlier, are dequantized into the other
+// buffer between the MFMAs of stage s.  Workgroups are numbered so that each
+// XCD (own L2) takes a contiguous range, walked in bands of 4 token tiles.
+// Rows past M or N and blocks past K load as zeros; rows past M or N are not
+// stored.
 #include "lsd_internal.h"
 #include "device_common.h"
 
@@ -37,7 +41,9 @@ constexpr int GS = GK + 8;              // LDS row stride (fp16 values)
 constexpr int NB = GK / kBlock;         // 16-value blocks per row per stage
 constexpr int SB = (GN * NB) / GT;      // blocks of one operand staged per thread per stage
 constexpr int kOutside = 0x7FFFFFF0;    // a byte offset past every buffer range (loads return 0)
+constexpr int kGroup = 4;               // token tiles per band of the workgroup order
 static_assert(GM == GN && SB == 2, "staging assumes square tiles and two blocks per thread");
+static_assert(GM == kLinTileRows && GK == kLinStage, "the tiled code layout is this kernel's staging order");
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -72,19 +78,28 @@ struct Stage {
   uint32_t s[SB];
 };
 
+template <bool kTiled>
 __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int K, int k0,
                                            int tid, Stage& st) {
 #pragma unroll
   for (int i = 0; i < SB; ++i) {
     const int b = tid + GT * i;
-    const int row = b / NB, kb = b % NB;
-    // blocks past K (a ragged last stage, or a stage past the end) read
-    // beyond the buffer range: zeros
-    const bool in = k0 + kBlock * kb < K;
-    const int oc = in ? row * (K / 2) + k0 / 2 + 8 * kb : kOutside;
-    const int os = in ? row * (K / kBlock) + k0 / kBlock + kb : kOutside;
-    st.c[i] = __builtin_amdgcn_raw_buffer_load_b64(rc, oc, 0, 0);
-    st.s[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, os, 0, 0);
+    if (kTiled) {
+      // stage k0 / GK of the tile is one contiguous chunk, block b at 8 b
+      // (codes) and b (scales); stages past the end lie beyond the range
+      const int stage = k0 / GK;
+      st.c[i] = __builtin_amdgcn_raw_buffer_load_b64(rc, stage * (GM * GK / 2) + 8 * b, 0, 0);
+      st.s[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, stage * (GM * NB) + b, 0, 0);
+    } else {
+      const int row = b / NB, kb = b % NB;
+      // blocks past K (a ragged last stage, or a stage past the end) read
+      // beyond the buffer range: zeros
+      const bool in = k0 + kBlock * kb < K;
+      const int oc = in ? row * (K / 2) + k0 / 2 + 8 * kb : kOutside;
+      const int os = in ? row * (K / kBlock) + k0 / kBlock + kb : kOutside;
+      st.c[i] = __builtin_amdgcn_raw_buffer_load_b64(rc, oc, 0, 0);
+      st.s[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, os, 0, 0);
+    }
   }
 }
 
@@ -139,6 +154,7 @@ __device__ __forceinline__ void stage_step(const uint16_t* wt, const uint16_t* x
   }
 }
 
+template <bool kTiled>
 __global__ __launch_bounds__(GT, 1) void nvfp4_gemm_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -147,20 +163,36 @@ __global__ __launch_bounds__(GT, 1) void nvfp4_gemm_kernel(GemmParams p) {
   const int l32 = lane & 31, hf = lane >> 5;
   const int lane_off = l32 * GS + 8 * hf;
 
-  // XCD-aware numbering (hardware id % 8 = XCD), then m-major tiles.
+  // XCD-aware numbering (hardware id % 8 = XCD: each XCD, with its own L2,
+  // takes a contiguous range), then bands of kGroup token tiles: consecutive
+  // workgroups walk the band's token tiles first, then its feature tiles, so
+  // the ~32 workgroups an XCD runs at once share 4 X tiles (kept in L2) and
+  // 8 W tiles.  A ragged last band is shorter.
   const int nblk = gridDim.x, bid = blockIdx.x;
   const int per = nblk >> 3, rem = nblk & 7, xcd = bid & 7;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
-  const int tm = logical / p.tiles_n, tn = logical - tm * p.tiles_n;
+  const int tiles_m = (p.M + GM - 1) / GM;
+  const int band = logical / (kGroup * p.tiles_n);
+  const int gh = tiles_m - band * kGroup < kGroup ? tiles_m - band * kGroup : kGroup;
+  const int in_band = logical - band * kGroup * p.tiles_n;
+  const int tm = band * kGroup + in_band % gh, tn = in_band / gh;
   const int m0 = tm * GM, n0 = tn * GN;
   const int K = p.K;
 
   const long long xrows = p.M - m0 < GM ? p.M - m0 : GM;
   const long long wrows = p.N - n0 < GN ? p.N - n0 : GN;
-  const __amdgpu_buffer_rsrc_t rxc = rsrc(p.xc + (size_t)m0 * (K / 2), xrows * (K / 2));
-  const __amdgpu_buffer_rsrc_t rxs = rsrc(p.xs + (size_t)m0 * (K / kBlock), xrows * (K / kBlock));
-  const __amdgpu_buffer_rsrc_t rwc = rsrc(p.wc + (size_t)n0 * (K / 2), wrows * (K / 2));
-  const __amdgpu_buffer_rsrc_t rws = rsrc(p.ws + (size_t)n0 * (K / kBlock), wrows * (K / kBlock));
+  const int nst = (K + GK - 1) / GK;
+  // a tiled operand's tile is nst contiguous chunks (zero padded); a
+  // row-major one is its rows
+  const size_t tc = (size_t)nst * (GM * GK / 2), ts = (size_t)nst * (GM * NB);
+  const __amdgpu_buffer_rsrc_t rxc = kTiled ? rsrc(p.xc + tm * tc, (long long)tc)
+                                            : rsrc(p.xc + (size_t)m0 * (K / 2), xrows * (K / 2));
+  const __amdgpu_buffer_rsrc_t rxs = kTiled ? rsrc(p.xs + tm * ts, (long long)ts)
+                                            : rsrc(p.xs + (size_t)m0 * (K / kBlock), xrows * (K / kBlock));
+  const __amdgpu_buffer_rsrc_t rwc = kTiled ? rsrc(p.wc + tn * tc, (long long)tc)
+                                            : rsrc(p.wc + (size_t)n0 * (K / 2), wrows * (K / 2));
+  const __amdgpu_buffer_rsrc_t rws = kTiled ? rsrc(p.ws + tn * ts, (long long)ts)
+                                            : rsrc(p.ws + (size_t)n0 * (K / kBlock), wrows * (K / kBlock));
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -171,12 +203,11 @@ __global__ __launch_bounds__(GT, 1) void nvfp4_gemm_kernel(GemmParams p) {
   // Register stages: stage s lives in set s % 2 from the top of step s - 2
   // (when it is loaded) to step s - 1 (when it is dequantized into LDS
   // buffer s % 2, which step s multiplies).
-  const int nst = (K + GK - 1) / GK;
   Stage w0, x0, w1, x1;
-  load_stage(rwc, rws, K, 0, tid, w0);
-  load_stage(rxc, rxs, K, 0, tid, x0);
-  load_stage(rwc, rws, K, GK, tid, w1);
-  load_stage(rxc, rxs, K, GK, tid, x1);
+  load_stage<kTiled>(rwc, rws, K, 0, tid, w0);
+  load_stage<kTiled>(rxc, rxs, K, 0, tid, x0);
+  load_stage<kTiled>(rwc, rws, K, GK, tid, w1);
+  load_stage<kTiled>(rxc, rxs, K, GK, tid, x1);
 #pragma unroll
   for (int i = 0; i < SB; ++i) {
     put_block(lw0, tid, i, w0);
@@ -185,13 +216,13 @@ __global__ __launch_bounds__(GT, 1) void nvfp4_gemm_kernel(GemmParams p) {
   __syncthreads();
 
   for (int s = 0; s < nst; s += 2) {
-    load_stage(rwc, rws, K, (s + 2) * GK, tid, w0);
-    load_stage(rxc, rxs, K, (s + 2) * GK, tid, x0);
+    load_stage<kTiled>(rwc, rws, K, (s + 2) * GK, tid, w0);
+    load_stage<kTiled>(rxc, rxs, K, (s + 2) * GK, tid, x0);
     stage_step(lw0, lx0, lw1, lx1, w1, x1, acc, lane_off, wn, wm, tid);
     __syncthreads();
     if (s + 1 < nst) {
-      load_stage(rwc, rws, K, (s + 3) * GK, tid, w1);
-      load_stage(rxc, rxs, K, (s + 3) * GK, tid, x1);
+      load_stage<kTiled>(rwc, rws, K, (s + 3) * GK, tid, w1);
+      load_stage<kTiled>(rxc, rxs, K, (s + 3) * GK, tid, x1);
       stage_step(lw1, lx1, lw0, lx0, w0, x0, acc, lane_off, wn, wm, tid);
       __syncthreads();
     }
@@ -230,7 +261,7 @@ __global__ __launch_bounds__(GT, 1) void nvfp4_gemm_kernel(GemmParams p) {
 }  // namespace
 
 hipError_t launch_nvfp4_linear(const uint8_t* xc, const uint8_t* xs, float gx, const uint8_t* wc, const uint8_t* ws,
-                               float gw, uint16_t* y, int M, int N, int K, hipStream_t stream) {
+                               float gw, uint16_t* y, int M, int N, int K, bool tiled, hipStream_t stream) {
   GemmParams p = {};
   p.xc = xc; p.xs = xs; p.wc = wc; p.ws = ws; p.y = y;
   p.M = M; p.N = N; p.K = K;
@@ -239,7 +270,10 @@ hipError_t launch_nvfp4_linear(const uint8_t* xc, const uint8_t* xs, float gx, c
   if (tiles <= 0 || tiles > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   p.tiles = (int)tiles;
   p.gscale = gx * gw;
-  hipLaunchKernelGGL(nvfp4_gemm_kernel, dim3((unsigned)tiles), dim3(GT), 0, stream, p);
+  if (tiled)
+    hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, dim3((unsigned)tiles), dim3(GT), 0, stream, p);
+  else
+    hipLaunchKernelGGL(nvfp4_gemm_kernel<false>, dim3((unsigned)tiles), dim3(GT), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -222,17 +222,11 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_kernel(const uint16_t* __
   *(uint16_t*)(scales + row * (kHeadDim / kBlock) + part * 2) = (uint16_t)(scode[0] | (scode[1] << 8));
 }
 
-// NVFP4 quantization of the rows of a linear layer's operand: thread i takes
-// values 16 i .. 16 i + 15 (one block of a row; rows are whole blocks), y =
-// RN32(x * r) with r = RN32(1 / g) for the tensor's global scale g, then the
-// block is quantized as above (no rotation).
-__global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_rows_kernel(const uint16_t* __restrict__ src,
-                                                                        uint8_t* __restrict__ codes,
-                                                                        uint8_t* __restrict__ scales,
-                                                                        long long nblocks, float r) {
-  const long long i = (long long)blockIdx.x * QUANT_THREADS + threadIdx.x;
-  if (i >= nblocks) return;
-  const u32x4* p = (const u32x4*)(src + 16 * i);
+// NVFP4 quantization of the rows of a linear layer's operand: y = RN32(x * r)
+// with r = RN32(1 / g) for the tensor's global scale g, then each block of 16
+// consecutive values of a row is quantized as above (no rotation).
+__device__ __forceinline__ u32x2 quant_linear_block(const uint16_t* src, float r, uint32_t& sc) {
+  const u32x4* p = (const u32x4*)src;
   const u32x4 a = p[0], b = p[1];
   float y[16];
 #pragma unroll
@@ -242,10 +236,48 @@ __global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_rows_kernel(const u
     y[8 + 2 * j] = __uint_as_float(b[j] << 16) * r;
     y[8 + 2 * j + 1] = __uint_as_float(b[j] & 0xFFFF0000u) * r;
   }
+  return quant_block16(y, sc);
+}
+
+// Row-major output: thread i takes block i (values 16 i .. 16 i + 15; rows
+// are whole blocks), codes at 8 i, scale at i.
+__global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_rows_kernel(const uint16_t* __restrict__ src,
+                                                                        uint8_t* __restrict__ codes,
+                                                                        uint8_t* __restrict__ scales,
+                                                                        long long nblocks, float r) {
+  const long long i = (long long)blockIdx.x * QUANT_THREADS + threadIdx.x;
+  if (i >= nblocks) return;
   uint32_t sc;
-  const u32x2 c = quant_block16(y, sc);
-  *(u32x2*)(codes + 8 * i) = c;
+  *(u32x2*)(codes + 8 * i) = quant_linear_block(src + 16 * i, r, sc);
   scales[i] = (uint8_t)sc;
+}
+
+// Tiled output (the product's load order): rows in tiles of kLinTileRows, K in
+// stages of kLinStage values; chunk (tile, stage) holds the tile's rows, each
+// row's kLinStage / 16 blocks contiguous (8 bytes of codes, 1 byte of scale
+// per block), chunks ordered tile-major.  Rows past the matrix and blocks past
+// K are written as zeros.  Workgroup (g, h) takes rows 16 g .. 16 g + 15 and
+// stages 4 h .. 4 h + 3; a wave takes 4 rows, lane l row l / 16 and block
+// l % 16 of the four stages: a wave reads 512 contiguous bytes of each of its
+// rows and writes, per stage, its 4 rows' 128 contiguous bytes of codes.
+__global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_tiled_kernel(const uint16_t* __restrict__ src,
+                                                                         uint8_t* __restrict__ codes,
+                                                                         uint8_t* __restrict__ scales,
+                                                                         long long rows, int kb_real, int stages,
+                                                                         float r) {
+  constexpr int kbs = kLinStage / kBlock;                 // blocks per row per stage
+  static_assert(QUANT_THREADS == 16 * 4 * kbs && kLinTileRows % 16 == 0, "16 rows x 4 stages per workgroup");
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int stage = blockIdx.y * 4 + (int)((threadIdx.x & 15) / kbs);
+  if (stage >= stages) return;
+  const int kg = stage * kbs + (int)(threadIdx.x % kbs);
+  u32x2 c = {0u, 0u};
+  uint32_t sc = 0u;
+  if (row < rows && kg < kb_real) c = quant_linear_block(src + (row * kb_real + kg) * kBlock, r, sc);
+  const long long chunk = (row / kLinTileRows) * stages + stage;
+  const int within = (int)(row % kLinTileRows) * kbs + (int)(threadIdx.x % kbs);
+  *(u32x2*)(codes + chunk * (kLinTileRows * kLinStage / 2) + 8 * within) = c;
+  scales[chunk * (kLinTileRows * kbs) + within] = (uint8_t)sc;
 }
 
 // ---------------------------------------------------------------- mean -------
@@ -453,9 +485,17 @@ void launch_quant(const uint16_t* src, const float* kmean, uint8_t* codes, uint8
 }  // namespace
 
 hipError_t launch_nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long rows, int cols,
-                                 float global_scale, hipStream_t stream) {
-  const long long nblocks = rows * (cols / kBlock);
+                                 float global_scale, bool tiled, hipStream_t stream) {
   const float r = (float)(1.0 / (double)global_scale);        // RN32(1/g)
+  if (tiled) {
+    const int stages = (cols + kLinStage - 1) / kLinStage;
+    const long long row_groups = (rows + kLinTileRows - 1) / kLinTileRows * (kLinTileRows / 16);
+    if (row_groups > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(nvfp4_quant_tiled_kernel, dim3((unsigned)row_groups, (unsigned)((stages + 3) / 4)),
+                       dim3(QUANT_THREADS), 0, stream, x, codes, scales, rows, cols / kBlock, stages, r);
+    return hipGetLastError();
+  }
+  const long long nblocks = rows * (cols / kBlock);
   const long long grid = (nblocks + QUANT_THREADS - 1) / QUANT_THREADS;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(nvfp4_quant_rows_kernel, dim3((unsigned)grid), dim3(QUANT_THREADS), 0, stream, x, codes, scales,

@@ -158,35 +158,51 @@ def test_bwd_fp4qk_argument_errors(lib):
 
 
 
+def test_nvfp4_buffer_sizes(lib):
+    assert lib.nvfp4_codes_bytes(109000, 5120, 0) == 109000 * 2560
+    assert lib.nvfp4_scales_bytes(109000, 5120, 0) == 109000 * 320
+    # tiled: 256-row tiles x 64-value stages, 8192 code and 1024 scale bytes each
+    assert lib.nvfp4_codes_bytes(109000, 5120, 1) == 426 * 80 * 8192
+    assert lib.nvfp4_scales_bytes(109000, 5120, 1) == 426 * 80 * 1024
+    assert lib.nvfp4_codes_bytes(1, 16, 1) == 8192 and lib.nvfp4_scales_bytes(257, 80, 1) == 2 * 2 * 1024
+    assert lib.nvfp4_codes_bytes(0, 16, 0) == 0 and lib.nvfp4_codes_bytes(4, 24, 1) == 0
+    assert lib.nvfp4_codes_bytes(4, 32, 2) == 0 and lib.nvfp4_scales_bytes(4, 32, -1) == 0
+
+
 def test_nvfp4_quantize_argument_errors(lib):
     f = lib.nvfp4_quantize
-    assert f(A, A, A, 0, 32, 1.0, N) == 2                               # rows
-    assert f(A, A, A, 4, 8, 1.0, N) == 2                                # cols < 16
-    assert f(A, A, A, 4, 40, 1.0, N) == 2                               # cols not a multiple of 16
-    assert f(A, A, A, 1 << 40, 16, 1.0, N) == 2                         # too many blocks for the grid
-    assert f(N, A, A, 4, 32, 1.0, N) == 1
-    assert f(A, A, N, 4, 32, 1.0, N) == 1
-    assert f(B, A, A, 4, 32, 1.0, N) == 4                               # x misaligned
-    assert f(A, B, A, 4, 32, 1.0, N) == 4                               # codes misaligned
-    assert f(A, A, A, 4, 32, 0.0, N) == 7
-    assert f(A, A, A, 4, 32, -2.0, N) == 7
-    assert f(A, A, A, 4, 32, float("inf"), N) == 7
-    assert f(A, A, A, 4, 32, 1e-45, N) == 7                             # 1/g overflows float32
+    for layout in (0, 1):
+        assert f(A, A, A, 0, 32, 1.0, layout, N) == 2                   # rows
+        assert f(A, A, A, 4, 8, 1.0, layout, N) == 2                    # cols < 16
+        assert f(A, A, A, 4, 40, 1.0, layout, N) == 2                   # cols not a multiple of 16
+        assert f(A, A, A, 1 << 40, 16, 1.0, layout, N) == 2             # too many blocks for the grid
+        assert f(N, A, A, 4, 32, 1.0, layout, N) == 1
+        assert f(A, A, N, 4, 32, 1.0, layout, N) == 1
+        assert f(B, A, A, 4, 32, 1.0, layout, N) == 4                   # x misaligned
+        assert f(A, B, A, 4, 32, 1.0, layout, N) == 4                   # codes misaligned
+        assert f(A, A, A, 4, 32, 0.0, layout, N) == 7
+        assert f(A, A, A, 4, 32, -2.0, layout, N) == 7
+        assert f(A, A, A, 4, 32, float("inf"), layout, N) == 7
+        assert f(A, A, A, 4, 32, 1e-45, layout, N) == 7                 # 1/g overflows float32
+    assert f(A, A, A, 4, 32, 1.0, 2, N) == 8                            # unknown layout
+    assert f(A, A, A, 4, 32, 1.0, -1, N) == 8
 
 
 def test_nvfp4_linear_argument_errors(lib):
     f = lib.nvfp4_linear
-    assert f(A, A, 1.0, A, A, 1.0, A, 0, 8, 64, N) == 2                 # M
-    assert f(A, A, 1.0, A, A, 1.0, A, 8, 0, 64, N) == 2                 # N
-    assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, 8, N) == 2                  # K < 16
-    assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, 72, N) == 2                 # K not a multiple of 16
-    assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, (1 << 20) + 16, N) == 2     # K too large
-    for i in (0, 1, 3, 4, 6):
-        args = [A, A, 1.0, A, A, 1.0, A]
-        args[i] = N
-        assert f(*args, 8, 8, 64, N) == 1, i
-    assert f(B, A, 1.0, A, A, 1.0, A, 8, 8, 64, N) == 4                 # x codes misaligned
-    assert f(A, A, 1.0, B, A, 1.0, A, 8, 8, 64, N) == 4
-    assert f(A, A, 1.0, A, A, 1.0, ctypes.c_void_p(0x100004), 8, 8, 64, N) == 4    # y needs 8 bytes
-    assert f(A, A, 0.0, A, A, 1.0, A, 8, 8, 64, N) == 7
-    assert f(A, A, 1.0, A, A, float("nan"), A, 8, 8, 64, N) == 7
+    for layout in (0, 1):
+        assert f(A, A, 1.0, A, A, 1.0, A, 0, 8, 64, layout, N) == 2     # M
+        assert f(A, A, 1.0, A, A, 1.0, A, 8, 0, 64, layout, N) == 2     # N
+        assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, 8, layout, N) == 2      # K < 16
+        assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, 72, layout, N) == 2     # K not a multiple of 16
+        assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, (1 << 20) + 16, layout, N) == 2    # K too large
+        for i in (0, 1, 3, 4, 6):
+            args = [A, A, 1.0, A, A, 1.0, A]
+            args[i] = N
+            assert f(*args, 8, 8, 64, layout, N) == 1, i
+        assert f(B, A, 1.0, A, A, 1.0, A, 8, 8, 64, layout, N) == 4     # x codes misaligned
+        assert f(A, A, 1.0, B, A, 1.0, A, 8, 8, 64, layout, N) == 4
+        assert f(A, A, 1.0, A, A, 1.0, ctypes.c_void_p(0x100004), 8, 8, 64, layout, N) == 4    # y needs 8 bytes
+        assert f(A, A, 0.0, A, A, 1.0, A, 8, 8, 64, layout, N) == 7
+        assert f(A, A, 1.0, A, A, float("nan"), A, 8, 8, 64, layout, N) == 7
+    assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, 64, 5, N) == 8              # unknown layout

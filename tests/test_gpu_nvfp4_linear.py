@@ -1,7 +1,10 @@
 """GPU parity of the NVFP4 W4A4 linear layer (nvfp4_quantize, nvfp4_linear)
 against the fp64 oracle (oracle.nvfp4_linear).
 
-The quantizer's codes and scales are compared bit for bit.  The product is
+The quantizer's codes and scales are compared bit for bit, in both code
+layouts (row-major, and the product's tiled load order: a plain permutation
+of the row-major bytes with zero padding, rebuilt here from the oracle's
+row-major codes).  The product is
 compared element by element within twice the error bound of the kernel's
 arithmetic (exact BF16 operands, fp32 sums, fp32 scaling, BF16 output);
 the oracle quantizes the same BF16 inputs itself, so no GPU value is an
@@ -52,24 +55,58 @@ def calibrated(bits):
     return float(amax / np.float32(E2M1_MAX * E4M3_MAX))
 
 
-def gpu_quantize(torch, bits, g):
+ROWS, TILED = 0, 1
+TILE_ROWS, STAGE = 256, 64
+
+
+def to_tiled(codes, scales):
+    """Row-major codes [R, K/2] and scales [R, K/16] -> the tiled byte order:
+    chunks (256-row tile, 64-value stage), tile-major, each holding its rows'
+    32 code bytes (4 scale bytes) in row order; zero padding."""
+    R, kc = codes.shape
+    T, S = -(-R // TILE_ROWS), -(-(2 * kc) // STAGE)
+    out = []
+    for a, per in ((codes, STAGE // 2), (scales, STAGE // 16)):
+        pad = np.zeros((T * TILE_ROWS, S * per), dtype=np.uint8)
+        pad[:R, :a.shape[1]] = a
+        out.append(pad.reshape(T, TILE_ROWS, S, per).transpose(0, 2, 1, 3).reshape(-1))
+    return out
+
+
+def from_tiled(codes, scales, R, K):
+    T, S = -(-R // TILE_ROWS), -(-K // STAGE)
+    out = []
+    for a, per, width in ((codes, STAGE // 2, K // 2), (scales, STAGE // 16, K // 16)):
+        full = a.reshape(T, S, TILE_ROWS, per).transpose(0, 2, 1, 3).reshape(T * TILE_ROWS, S * per)
+        out.append(full[:R, :width])
+    return out
+
+
+def gpu_quantize(torch, bits, g, layout=ROWS):
     from long_sequence_dense_amd import binding
     x = bf16_dev(torch, bits)
     rows, cols = bits.shape
-    codes = torch.full((rows, cols // 2), 0xA5, dtype=torch.uint8, device="cuda")
-    scales = torch.full((rows, cols // 16), 0xA5, dtype=torch.uint8, device="cuda")
-    binding.nvfp4_quantize(x, g, codes, scales)
+    cshape = (rows, cols // 2) if layout == ROWS else (binding.nvfp4_codes_bytes(rows, cols, layout),)
+    sshape = (rows, cols // 16) if layout == ROWS else (binding.nvfp4_scales_bytes(rows, cols, layout),)
+    codes = torch.full(cshape, 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full(sshape, 0xA5, dtype=torch.uint8, device="cuda")
+    binding.nvfp4_quantize(x, g, codes, scales, layout=layout)
     torch.cuda.synchronize()
     return codes, scales
 
 
-def check_codes(tag, got_c, got_s, bits, g):
+def check_codes(tag, got_c, got_s, bits, g, layout=ROWS):
+    """Compare with the oracle's codes (in the layout's byte order); returns
+    the oracle's row-major codes and scales."""
     want_c, want_s = ref.quantize(inputs.bf16_bits_to_f32(bits), g)
+    rc, rs = want_c, want_s
+    if layout == TILED:
+        want_c, want_s = to_tiled(want_c, want_s)
     gc, gs = got_c.cpu().numpy(), got_s.cpu().numpy()
     nc, ns = int(np.sum(gc != want_c)), int(np.sum(gs != want_s))
     say("  %-28s codes %d/%d differ, scales %d/%d differ" % (tag, nc, gc.size, ns, gs.size))
     assert nc == 0 and ns == 0
-    return want_c, want_s
+    return rc, rs
 
 
 QUANT_CASES = [
@@ -83,14 +120,29 @@ QUANT_CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", [ROWS, TILED])
 @pytest.mark.parametrize("rows,cols,seed,gsel", QUANT_CASES)
-def test_quantize_bit_exact(torch, rows, cols, seed, gsel):
+def test_quantize_bit_exact(torch, rows, cols, seed, gsel, layout):
     bits = inputs.linear_operand("x", rows, cols, seed)
     g = {"one": 1.0, "calibrated": calibrated(bits), "pow2": 0.125, "clip": calibrated(bits) / 50.0,
          "odd": float(np.float32(0.0123456))}[gsel]
-    say("case quantize rows=%d cols=%d seed=%d g=%s (%r)" % (rows, cols, seed, gsel, g))
-    c, s = gpu_quantize(torch, bits, g)
-    check_codes("x %dx%d" % (rows, cols), c, s, bits, g)
+    say("case quantize rows=%d cols=%d seed=%d g=%s (%r) layout=%d" % (rows, cols, seed, gsel, g, layout))
+    c, s = gpu_quantize(torch, bits, g, layout)
+    check_codes("x %dx%d" % (rows, cols), c, s, bits, g, layout)
+
+
+def test_tiled_layout_is_a_permutation():
+    # the test's own re-layout: round trip, padding zero, chunk placement
+    rng = np.random.default_rng(3)
+    c = rng.integers(0, 256, (300, 40), dtype=np.uint8)
+    s_ = rng.integers(0, 127, (300, 5), dtype=np.uint8)
+    tc, ts = to_tiled(c, s_)
+    assert tc.size == 2 * 2 * 8192 and ts.size == 2 * 2 * 1024
+    back_c, back_s = from_tiled(tc, ts, 300, 80)
+    assert np.array_equal(back_c, c) and np.array_equal(back_s, s_)
+    assert np.array_equal(tc[8192:8192 + 32][:8], c[0, 32:40])          # tile 0, stage 1, row 0
+    assert np.all(tc[8192 + 32 * 0 + 8:8192 + 32] == 0)                  # K padding of stage 1
+    assert np.all(tc[3 * 8192 + 32 * 44:] == 0)                          # rows past 300 in tile 1
 
 
 def compare(tag, got, want, bound):
@@ -117,59 +169,77 @@ LINEAR_CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", [ROWS, TILED])
 @pytest.mark.parametrize("M,N,K", LINEAR_CASES)
-def test_linear_small_full(torch, M, N, K):
+def test_linear_small_full(torch, M, N, K, layout):
     from long_sequence_dense_amd import binding
-    say("case linear M=%d N=%d K=%d" % (M, N, K))
+    say("case linear M=%d N=%d K=%d layout=%d" % (M, N, K, layout))
     xb = inputs.linear_operand("x", M, K, 20 + M)
     wb = inputs.linear_operand("w", N, K, 30 + N)
     gx, gw = calibrated(xb), calibrated(wb)
-    xc, xs = gpu_quantize(torch, xb, gx)
-    wc, ws = gpu_quantize(torch, wb, gw)
-    rxc, rxs = check_codes("x", xc, xs, xb, gx)
-    rwc, rws = check_codes("w", wc, ws, wb, gw)
+    xc, xs = gpu_quantize(torch, xb, gx, layout)
+    wc, ws = gpu_quantize(torch, wb, gw, layout)
+    rxc, rxs = check_codes("x", xc, xs, xb, gx, layout)
+    rwc, rws = check_codes("w", wc, ws, wb, gw, layout)
     y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
-    binding.nvfp4_linear(xc, xs, gx, wc, ws, gw, y)
+    binding.nvfp4_linear(xc, xs, gx, wc, ws, gw, y, layout=layout, M=M, N=N, K=K)
     torch.cuda.synchronize()
     want = ref.linear(rxc, rxs, gx, rwc, rws, gw)
     bound = ref.linear_bound(rxc, rxs, gx, rwc, rws, gw)
     compare("y %dx%dx%d" % (M, N, K), to_f64(torch, y), want, bound)
 
 
-def test_linear_deterministic(torch):
+def test_linear_deterministic_and_layouts_agree(torch):
     from long_sequence_dense_amd import binding
     M, N, K = 600, 520, 640
     say("case linear deterministic M=%d N=%d K=%d" % (M, N, K))
-    xc, xs = gpu_quantize(torch, inputs.linear_operand("x", M, K, 41), 0.01)
-    wc, ws = gpu_quantize(torch, inputs.linear_operand("w", N, K, 42), 0.001)
+    xb, wb = inputs.linear_operand("x", M, K, 41), inputs.linear_operand("w", N, K, 42)
+    xc, xs = gpu_quantize(torch, xb, 0.01)
+    wc, ws = gpu_quantize(torch, wb, 0.001)
     a = binding.nvfp4_linear(xc, xs, 0.01, wc, ws, 0.001)
     b = binding.nvfp4_linear(xc, xs, 0.01, wc, ws, 0.001)
+    txc, txs = gpu_quantize(torch, xb, 0.01, TILED)
+    twc, tws = gpu_quantize(torch, wb, 0.001, TILED)
+    t = binding.nvfp4_linear(txc, txs, 0.01, twc, tws, 0.001, layout=TILED, M=M, N=N, K=K)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # the same products summed in the same order: identical bits
+    assert torch.equal(a.view(torch.int16), t.view(torch.int16))
 
 
 FULL_M, FULL_N, FULL_K = 109000, 5120, 5120
 
 
-def test_linear_full_size(torch):
-    """Full-size projection as the benchmark runs it: all weight codes bit
-    exact, sampled token rows' codes bit exact and their outputs within the
-    bound."""
+@pytest.mark.parametrize("layout", [TILED, ROWS])
+def test_linear_full_size(torch, layout):
+    """Full-size projection as the benchmark runs it (tiled) and row-major:
+    all weight codes bit exact, sampled token rows' codes bit exact and their
+    outputs within the bound."""
     from long_sequence_dense_amd import binding
-    say("case linear full M=%d N=%d K=%d (generate)" % (FULL_M, FULL_N, FULL_K))
-    xb = inputs.linear_operand("x", FULL_M, FULL_K, 7)
-    wb = inputs.linear_operand("w", FULL_N, FULL_K, 8)
+    M, N, K = FULL_M, FULL_N, FULL_K
+    say("case linear full M=%d N=%d K=%d layout=%d (generate)" % (M, N, K, layout))
+    xb = inputs.linear_operand("x", M, K, 7)
+    wb = inputs.linear_operand("w", N, K, 8)
     gx, gw = calibrated(xb), calibrated(wb)
-    xc, xs = gpu_quantize(torch, xb, gx)
+    xc, xs = gpu_quantize(torch, xb, gx, layout)
     del xb
-    wc, ws = gpu_quantize(torch, wb, gw)
-    rwc, rws = check_codes("w all rows", wc, ws, wb, gw)
-    y = binding.nvfp4_linear(xc, xs, gx, wc, ws, gw)
+    wc, ws = gpu_quantize(torch, wb, gw, layout)
+    rwc, rws = check_codes("w all rows", wc, ws, wb, gw, layout)
+    y = binding.nvfp4_linear(xc, xs, gx, wc, ws, gw, layout=layout, M=M, N=N, K=K)
     torch.cuda.synchronize()
-    rows = inputs.sample_rows(FULL_M, 48, seed=77, tiles=(256,))
-    xr = inputs.linear_operand("x", FULL_M, FULL_K, 7, row_ids=rows)
-    idx = torch.from_numpy(rows).cuda()
-    rxc, rxs = check_codes("x sampled rows", xc.index_select(0, idx), xs.index_select(0, idx), xr, gx)
+    rows = inputs.sample_rows(M, 48, seed=77, tiles=(256,))
+    xr = inputs.linear_operand("x", M, K, 7, row_ids=rows)
+    if layout == TILED:
+        gxc, gxs = from_tiled(xc.cpu().numpy(), xs.cpu().numpy(), M, K)
+        gxc, gxs = gxc[rows], gxs[rows]
+    else:
+        idx = torch.from_numpy(rows).cuda()
+        gxc, gxs = xc.index_select(0, idx).cpu().numpy(), xs.index_select(0, idx).cpu().numpy()
+    rxc, rxs = ref.quantize(inputs.bf16_bits_to_f32(xr), gx)
+    nc, ns = int(np.sum(gxc != rxc)), int(np.sum(gxs != rxs))
+    say("  %-28s codes %d/%d differ, scales %d/%d differ" % ("x sampled rows", nc, rxc.size, ns, rxs.size))
+    assert nc == 0 and ns == 0
     want = ref.linear(rxc, rxs, gx, rwc, rws, gw)
     bound = ref.linear_bound(rxc, rxs, gx, rwc, rws, gw)
+    idx = torch.from_numpy(rows).cuda()
     compare("y sampled rows", to_f64(torch, y.index_select(0, idx)), want, bound)
