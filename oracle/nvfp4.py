@@ -11,8 +11,8 @@ caption on the yuxiaoba review ("Decoding can cost more than denoising") shows
 a 16-value key block whose small entry rounds to zero.
 
 The pages give no numerics for these steps, so this module fixes one procedure
-(each reading is listed in the design doc).  For head h and token row l, P1-P2 on K
-only:
+(one plain reading of each step, stated below).  For head h and token row l,
+P1-P2 on K only:
 
 P0  x_c = the BF16 input as a real number (exact).
 P1  kbar_c = RN32( RN64(S_c) / L ),  S_c = exact sum over the L tokens of

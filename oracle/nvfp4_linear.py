@@ -6,7 +6,7 @@ weights and activations, one 8-bit scale per 16 values; activation scales are
 static, set per layer from calibration (a clipping level).  The block format is
 the one of section "FP4 attention" (E2M1 values, E4M3 scale per 16).
 
-Readings (the pages give no numerics; listed in the design doc):
+Readings (the pages give no numerics for these steps):
   * a tensor has one float32 global scale g > 0 besides its block scales: the
     quantizer sees x' = RN32(x * r) with r = RN32(1 / g) (one multiply per
     value; equal to RN32(x / g) when g is a power of two), quantizes x' by
