@@ -198,7 +198,7 @@ def main():
     ap.add_argument("--only", choices=["all", "bf16"], default="all",
                     help="bf16: time only attn_fwd_bf16 (for profiling runs)")
     ap.add_argument("--no-bwd", action="store_true",
-                    help="skip the extra (not in value) timing of attn_bwd_bf16")
+                    help="skip the extra (not in value) timing of attn_bwd_bf16 and attn_bwd_fp4qk")
     ap.add_argument("--no-linear", action="store_true",
                     help="skip the extra (not in value) timing of the NVFP4 linear layer")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -338,7 +338,22 @@ def main():
                                   "flop_convention": "2.5 x forward (5 of the 2HL^2d products); the kernels "
                                                      "compute 7 (S and dP again for dQ)",
                                   "in_value": False}
-        del grads, dout, bws
+        # The training-time FP4 backward on the FP4 path's tensors (the codes
+        # of the step's prep, its forward's output and LSE): 1 warm-up + 2 calls.
+        log("timing attn_bwd_fp4qk (2 calls) ...")
+        binding.attn_fwd_fp4qk(prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], x5["v"], o5,
+                               lse, cfg5.scale, stream)
+        fws = torch.empty(binding.attn_bwd_fp4qk_workspace_bytes(H, L, d), dtype=torch.uint8, device=dev)
+        t_fb = time_calls(torch, stream, lambda: binding.attn_bwd_fp4qk(
+            prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], x5["v"], o5, lse, dout, *grads,
+            softmax_scale=cfg5.scale, workspace=fws, stream=stream), n=2)
+        fb = 2.5 * fl / (t_fb * 1e-3) / 1e12
+        paths["attn_bwd_fp4qk"] = {"ms": round(t_fb, 3), "TFLOP/s": round(fb, 1),
+                                   "frac_of_peak": round(fb / PEAK_BF16_TFLOPS, 4),
+                                   "flop_convention": "as attn_bwd_bf16; the time also covers the exact "
+                                                      "dequantization of Q, K and the rotation of dQ, dK back",
+                                   "in_value": False}
+        del grads, dout, bws, fws
     if args.only != "bf16" and not args.no_linear:
         # Extra path, outside the step and its value: one NVFP4 W4A4 linear of
         # the same transformer at the 40 x 128 hidden size, over the clip's
