@@ -21,6 +21,7 @@ import numpy as np
 import pytest
 
 from long_sequence_dense_amd import inputs
+from nvfp4_layout import from_tiled, to_tiled
 from oracle import nvfp4_linear as ref
 
 pytestmark = pytest.mark.gpu
@@ -56,32 +57,6 @@ def calibrated(bits):
 
 
 ROWS, TILED = 0, 1
-TILE_ROWS, STAGE = 256, 64
-
-
-def to_tiled(codes, scales):
-    """Row-major codes [R, K/2] and scales [R, K/16] -> the tiled byte order:
-    chunks (256-row tile, 64-value stage), tile-major, each holding its rows'
-    32 code bytes (4 scale bytes) in row order; zero padding."""
-    R, kc = codes.shape
-    T, S = -(-R // TILE_ROWS), -(-(2 * kc) // STAGE)
-    out = []
-    for a, per in ((codes, STAGE // 2), (scales, STAGE // 16)):
-        pad = np.zeros((T * TILE_ROWS, S * per), dtype=np.uint8)
-        pad[:R, :a.shape[1]] = a
-        out.append(pad.reshape(T, TILE_ROWS, S, per).transpose(0, 2, 1, 3).reshape(-1))
-    return out
-
-
-def from_tiled(codes, scales, R, K):
-    T, S = -(-R // TILE_ROWS), -(-K // STAGE)
-    out = []
-    for a, per, width in ((codes, STAGE // 2, K // 2), (scales, STAGE // 16, K // 16)):
-        full = a.reshape(T, S, TILE_ROWS, per).transpose(0, 2, 1, 3).reshape(T * TILE_ROWS, S * per)
-        out.append(full[:R, :width])
-    return out
-
-
 def gpu_quantize(torch, bits, g, layout=ROWS):
     from long_sequence_dense_amd import binding
     x = bf16_dev(torch, bits)
@@ -129,20 +104,6 @@ def test_quantize_bit_exact(torch, rows, cols, seed, gsel, layout):
     say("case quantize rows=%d cols=%d seed=%d g=%s (%r) layout=%d" % (rows, cols, seed, gsel, g, layout))
     c, s = gpu_quantize(torch, bits, g, layout)
     check_codes("x %dx%d" % (rows, cols), c, s, bits, g, layout)
-
-
-def test_tiled_layout_is_a_permutation():
-    # the test's own re-layout: round trip, padding zero, chunk placement
-    rng = np.random.default_rng(3)
-    c = rng.integers(0, 256, (300, 40), dtype=np.uint8)
-    s_ = rng.integers(0, 127, (300, 5), dtype=np.uint8)
-    tc, ts = to_tiled(c, s_)
-    assert tc.size == 2 * 2 * 8192 and ts.size == 2 * 2 * 1024
-    back_c, back_s = from_tiled(tc, ts, 300, 80)
-    assert np.array_equal(back_c, c) and np.array_equal(back_s, s_)
-    assert np.array_equal(tc[8192:8192 + 32][:8], c[0, 32:40])          # tile 0, stage 1, row 0
-    assert np.all(tc[8192 + 32 * 0 + 8:8192 + 32] == 0)                  # K padding of stage 1
-    assert np.all(tc[3 * 8192 + 32 * 44:] == 0)                          # rows past 300 in tile 1
 
 
 def compare(tag, got, want, bound):
