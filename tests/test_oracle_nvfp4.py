@@ -3,8 +3,9 @@
 Method: "Pika H3 Flex in FastVideo: 7x Faster, and Near Real Time in 4-bit",
 section "FP4 attention" (mean-key subtraction, a shared orthonormal Hadamard
 rotation of Q and K, E2M1 values with one E4M3 scale per 16 channels and a unit
-global scale); the 16-value block with a small entry rounding to zero is the
-figure on the yuxiaoba review "Decoding can cost more than denoising".
+global scale); the 16-value block with a small entry rounding to zero is of the
+kind the figure on the yuxiaoba review "Decoding can cost more than denoising"
+shows (its caption gives no values, so the block is constructed here).
 
 Everything the oracle computes is compared with something other than itself:
 bit-field definitions and torch's float8 decoder for the codecs, Fraction
