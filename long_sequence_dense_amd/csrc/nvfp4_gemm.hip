@@ -23,7 +23,9 @@
 // advances 64 at a time through double-buffered LDS tiles (row stride 144 B:
 // the operand reads are free of bank conflicts); the codes of stage s + 1,
 // loaded into registers one step earlier, are dequantized into the other
-// buffer between the MFMAs of stage s.  Workgroups are numbered so that each
+// buffer between the MFMAs of stage s.  With tiled codes a stage of a tile
+// is one contiguous chunk, and each thread loads two adjacent blocks per
+// operand with one 16-byte load (row-major codes: one load per block).  Workgroups are numbered so that each
 // XCD (own L2) takes a contiguous range, walked in bands of 4 token tiles.
 // Rows past M or N and blocks past K load as zeros; rows past M or N are not
 // stored.
@@ -71,29 +73,46 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long lo
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-// Codes and scales of one operand's stage, this thread's share: block
-// b = tid + GT * i covers row b / NB, values 16 * (b % NB) .. +15 of the stage.
-struct Stage {
-  u32x2 c[SB];
-  uint32_t s[SB];
-};
+// Exact dequantization of one 16-value block (codes w0, w1; E4M3 scale code
+// c, sign clear) into row `row`, block `kb` of an LDS tile: an E2M1 value
+// times an E4M3 scale has at most 6 significant bits and lies in [2^-10,
+// 2688] when nonzero, so it is exact in FP16 (normal range) as well as BF16.
+// The packed FP16 multiply takes two values per instruction.
+__device__ __forceinline__ void put_values(uint16_t* tile, int row, int kb, uint32_t w0, uint32_t w1, uint32_t c) {
+  // E4M3 scale code to FP16: the bits c << 7 read as FP16 carry the exponent
+  // and mantissa fields (biases 15 vs 7, codes with a zero exponent land on
+  // FP16 subnormals of the same form), times 2^8 exact.
+  const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)((c & 0x7Fu) << 7)) * (_Float16)256.0f;
+  const f16x2 s2 = {sh, sh};
+  u32x4 lo, hi;
+  lo[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0) * s2);
+  lo[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1) * s2);
+  lo[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2) * s2);
+  lo[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3) * s2);
+  hi[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 0) * s2);
+  hi[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 1) * s2);
+  hi[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 2) * s2);
+  hi[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3) * s2);
+  *(u32x4*)(tile + row * GS + kBlock * kb) = lo;
+  *(u32x4*)(tile + row * GS + kBlock * kb + 8) = hi;
+}
 
-template <bool kTiled>
-__device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int K, int k0,
-                                           int tid, Stage& st) {
+// Staging of one operand's stage, row-major codes: thread t stages blocks
+// b = t + GT * i (i < SB), row b / NB, values 16 (b % NB) .. +15 of the stage,
+// each from its own 8-byte code load and 1-byte scale load.  Blocks past K (a
+// ragged last stage, or a stage past the end) read beyond the buffer range:
+// zeros.
+struct RowsStaging {
+  struct Stage {
+    u32x2 c[SB];
+    uint32_t s[SB];
+  };
+  __device__ static __forceinline__ void load(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int K, int k0,
+                                              int tid, Stage& st) {
 #pragma unroll
-  for (int i = 0; i < SB; ++i) {
-    const int b = tid + GT * i;
-    if (kTiled) {
-      // stage k0 / GK of the tile is one contiguous chunk, block b at 8 b
-      // (codes) and b (scales); stages past the end lie beyond the range
-      const int stage = k0 / GK;
-      st.c[i] = __builtin_amdgcn_raw_buffer_load_b64(rc, stage * (GM * GK / 2) + 8 * b, 0, 0);
-      st.s[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, stage * (GM * NB) + b, 0, 0);
-    } else {
+    for (int i = 0; i < SB; ++i) {
+      const int b = tid + GT * i;
       const int row = b / NB, kb = b % NB;
-      // blocks past K (a ragged last stage, or a stage past the end) read
-      // beyond the buffer range: zeros
       const bool in = k0 + kBlock * kb < K;
       const int oc = in ? row * (K / 2) + k0 / 2 + 8 * kb : kOutside;
       const int os = in ? row * (K / kBlock) + k0 / kBlock + kb : kOutside;
@@ -101,32 +120,33 @@ __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rc, __amdgpu_b
       st.s[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, os, 0, 0);
     }
   }
-}
+  __device__ static __forceinline__ void put(uint16_t* tile, int tid, int i, const Stage& st) {
+    const int b = tid + GT * i;
+    put_values(tile, b / NB, b % NB, st.c[i][0], st.c[i][1], st.s[i] & 0xFFu);
+  }
+};
 
-// Exact dequantization of block i of a stage into an LDS tile: an E2M1 value
-// times an E4M3 scale has at most 6 significant bits and lies in [2^-10,
-// 2688] when nonzero, so it is exact in FP16 (normal range) as well as BF16.
-// The packed FP16 multiply takes two values per instruction.
-__device__ __forceinline__ void put_block(uint16_t* tile, int tid, int i, const Stage& st) {
-  const int b = tid + GT * i;
-  const int row = b / NB, kb = b % NB;
-  // E4M3 scale code c (sign clear) to FP16: the bits c << 7 read as FP16
-  // carry the exponent and mantissa fields (biases 15 vs 7, codes with a zero
-  // exponent land on FP16 subnormals of the same form), times 2^8 exact.
-  const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)((st.s[i] & 0x7Fu) << 7)) * (_Float16)256.0f;
-  const f16x2 s2 = {sh, sh};
-  u32x4 lo, hi;
-  lo[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][0], 1.0f, 0) * s2);
-  lo[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][0], 1.0f, 1) * s2);
-  lo[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][0], 1.0f, 2) * s2);
-  lo[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][0], 1.0f, 3) * s2);
-  hi[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][1], 1.0f, 0) * s2);
-  hi[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][1], 1.0f, 1) * s2);
-  hi[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][1], 1.0f, 2) * s2);
-  hi[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(st.c[i][1], 1.0f, 3) * s2);
-  *(u32x4*)(tile + row * GS + kBlock * kb) = lo;
-  *(u32x4*)(tile + row * GS + kBlock * kb + 8) = hi;
-}
+// Staging of one operand's stage, tiled codes: the stage is one contiguous
+// chunk (blocks in row order, 8 code bytes and 1 scale byte each), and thread
+// t stages the adjacent blocks 2t and 2t + 1 (row t / 2, blocks 2 (t % 2) and
+// 2 (t % 2) + 1) with one 16-byte code load and one 2-byte scale load.  Stages
+// past the end of K lie beyond the buffer range: zeros.
+struct TiledStaging {
+  struct Stage {
+    u32x4 c;
+    uint32_t s;
+  };
+  __device__ static __forceinline__ void load(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int, int k0,
+                                              int tid, Stage& st) {
+    const int stage = k0 / GK;
+    st.c = __builtin_amdgcn_raw_buffer_load_b128(rc, stage * (GM * GK / 2) + 16 * tid, 0, 0);
+    st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, stage * (GM * NB) + 2 * tid, 0, 0);
+  }
+  __device__ static __forceinline__ void put(uint16_t* tile, int tid, int i, const Stage& st) {
+    put_values(tile, tid >> 1, 2 * (tid & 1) + i, st.c[2 * i], st.c[2 * i + 1], (st.s >> (8 * i)) & 0xFFu);
+  }
+};
+static_assert(GT * 2 == GM * NB, "tiled staging gives every thread two blocks of each operand's stage");
 
 __device__ __forceinline__ f16x8 operand(const uint16_t* tile, int lane_off, int row0, int ks) {
   return __builtin_bit_cast(f16x8, *(const u16x8*)(tile + row0 * GS + lane_off + 16 * ks));
@@ -134,8 +154,10 @@ __device__ __forceinline__ f16x8 operand(const uint16_t* tile, int lane_off, int
 
 // One K stage: multiply the tiles in (wt, xt) while the codes in (dw, dx),
 // the next stage, are dequantized into (wd, xd), one block per 16-wide step.
+template <class SP>
 __device__ __forceinline__ void stage_step(const uint16_t* wt, const uint16_t* xt, uint16_t* wd, uint16_t* xd,
-                                           const Stage& dw, const Stage& dx, f32x16 (&acc)[4][2], int lane_off,
+                                           const typename SP::Stage& dw, const typename SP::Stage& dx,
+                                           f32x16 (&acc)[4][2], int lane_off,
                                            int wn, int wm, int tid) {
 #pragma unroll
   for (int ks = 0; ks < GK / 16; ++ks) {
@@ -149,12 +171,12 @@ __device__ __forceinline__ void stage_step(const uint16_t* wt, const uint16_t* x
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
-    if (ks < 2) put_block(wd, tid, ks, dw);
-    else put_block(xd, tid, ks - 2, dx);
+    if (ks < 2) SP::put(wd, tid, ks, dw);
+    else SP::put(xd, tid, ks - 2, dx);
   }
 }
 
-template <bool kTiled>
+template <class SP, bool kTiled>
 __global__ __launch_bounds__(GT, 1) void nvfp4_gemm_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -203,27 +225,27 @@ __global__ __launch_bounds__(GT, 1) void nvfp4_gemm_kernel(GemmParams p) {
   // Register stages: stage s lives in set s % 2 from the top of step s - 2
   // (when it is loaded) to step s - 1 (when it is dequantized into LDS
   // buffer s % 2, which step s multiplies).
-  Stage w0, x0, w1, x1;
-  load_stage<kTiled>(rwc, rws, K, 0, tid, w0);
-  load_stage<kTiled>(rxc, rxs, K, 0, tid, x0);
-  load_stage<kTiled>(rwc, rws, K, GK, tid, w1);
-  load_stage<kTiled>(rxc, rxs, K, GK, tid, x1);
+  typename SP::Stage w0, x0, w1, x1;
+  SP::load(rwc, rws, K, 0, tid, w0);
+  SP::load(rxc, rxs, K, 0, tid, x0);
+  SP::load(rwc, rws, K, GK, tid, w1);
+  SP::load(rxc, rxs, K, GK, tid, x1);
 #pragma unroll
   for (int i = 0; i < SB; ++i) {
-    put_block(lw0, tid, i, w0);
-    put_block(lx0, tid, i, x0);
+    SP::put(lw0, tid, i, w0);
+    SP::put(lx0, tid, i, x0);
   }
   __syncthreads();
 
   for (int s = 0; s < nst; s += 2) {
-    load_stage<kTiled>(rwc, rws, K, (s + 2) * GK, tid, w0);
-    load_stage<kTiled>(rxc, rxs, K, (s + 2) * GK, tid, x0);
-    stage_step(lw0, lx0, lw1, lx1, w1, x1, acc, lane_off, wn, wm, tid);
+    SP::load(rwc, rws, K, (s + 2) * GK, tid, w0);
+    SP::load(rxc, rxs, K, (s + 2) * GK, tid, x0);
+    stage_step<SP>(lw0, lx0, lw1, lx1, w1, x1, acc, lane_off, wn, wm, tid);
     __syncthreads();
     if (s + 1 < nst) {
-      load_stage<kTiled>(rwc, rws, K, (s + 3) * GK, tid, w1);
-      load_stage<kTiled>(rxc, rxs, K, (s + 3) * GK, tid, x1);
-      stage_step(lw1, lx1, lw0, lx0, w0, x0, acc, lane_off, wn, wm, tid);
+      SP::load(rwc, rws, K, (s + 3) * GK, tid, w1);
+      SP::load(rxc, rxs, K, (s + 3) * GK, tid, x1);
+      stage_step<SP>(lw1, lx1, lw0, lx0, w0, x0, acc, lane_off, wn, wm, tid);
       __syncthreads();
     }
   }
@@ -271,9 +293,9 @@ hipError_t launch_nvfp4_linear(const uint8_t* xc, const uint8_t* xs, float gx, c
   p.tiles = (int)tiles;
   p.gscale = gx * gw;
   if (tiled)
-    hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, dim3((unsigned)tiles), dim3(GT), 0, stream, p);
+    hipLaunchKernelGGL((nvfp4_gemm_kernel<TiledStaging, true>), dim3((unsigned)tiles), dim3(GT), 0, stream, p);
   else
-    hipLaunchKernelGGL(nvfp4_gemm_kernel<false>, dim3((unsigned)tiles), dim3(GT), 0, stream, p);
+    hipLaunchKernelGGL((nvfp4_gemm_kernel<RowsStaging, false>), dim3((unsigned)tiles), dim3(GT), 0, stream, p);
   return hipGetLastError();
 }
 
