@@ -225,9 +225,7 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_kernel(const uint16_t* __
 // NVFP4 quantization of the rows of a linear layer's operand: y = RN32(x * r)
 // with r = RN32(1 / g) for the tensor's global scale g, then each block of 16
 // consecutive values of a row is quantized as above (no rotation).
-__device__ __forceinline__ u32x2 quant_linear_block(const uint16_t* src, float r, uint32_t& sc) {
-  const u32x4* p = (const u32x4*)src;
-  const u32x4 a = p[0], b = p[1];
+__device__ __forceinline__ u32x2 quant_linear_raw(u32x4 a, u32x4 b, float r, uint32_t& sc) {
   float y[16];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -237,6 +235,11 @@ __device__ __forceinline__ u32x2 quant_linear_block(const uint16_t* src, float r
     y[8 + 2 * j + 1] = __uint_as_float(b[j] & 0xFFFF0000u) * r;
   }
   return quant_block16(y, sc);
+}
+
+__device__ __forceinline__ u32x2 quant_linear_block(const uint16_t* src, float r, uint32_t& sc) {
+  const u32x4* p = (const u32x4*)src;
+  return quant_linear_raw(p[0], p[1], r, sc);
 }
 
 // Row-major output: thread i takes block i (values 16 i .. 16 i + 15; rows
@@ -256,28 +259,47 @@ __global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_rows_kernel(const u
 // stages of kLinStage values; chunk (tile, stage) holds the tile's rows, each
 // row's kLinStage / 16 blocks contiguous (8 bytes of codes, 1 byte of scale
 // per block), chunks ordered tile-major.  Rows past the matrix and blocks past
-// K are written as zeros.  Workgroup (g, h) takes rows 16 g .. 16 g + 15 and
-// stages 4 h .. 4 h + 3; a wave takes 4 rows, lane l row l / 16 and block
-// l % 16 of the four stages: a wave reads 512 contiguous bytes of each of its
-// rows and writes, per stage, its 4 rows' 128 contiguous bytes of codes.
+// K are written as zeros.  Workgroup g * ceil(stages / 4) + h takes rows
+// 32 g .. 32 g + 31 and stages 4 h .. 4 h + 3; lane l of wave w takes row 32 g + 8 w + l / 8 and the
+// two adjacent blocks 2 (l % 8) and 2 (l % 8) + 1 of the four stages: a wave
+// reads 512 contiguous bytes of each of its 8 rows and writes, per stage and
+// row, 32 contiguous bytes of codes with two 16-byte stores.
 __global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_tiled_kernel(const uint16_t* __restrict__ src,
                                                                          uint8_t* __restrict__ codes,
                                                                          uint8_t* __restrict__ scales,
                                                                          long long rows, int kb_real, int stages,
                                                                          float r) {
   constexpr int kbs = kLinStage / kBlock;                 // blocks per row per stage
-  static_assert(QUANT_THREADS == 16 * 4 * kbs && kLinTileRows % 16 == 0, "16 rows x 4 stages per workgroup");
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int stage = blockIdx.y * 4 + (int)((threadIdx.x & 15) / kbs);
+  static_assert(QUANT_THREADS == 32 * 8 && kbs == 4 && kLinTileRows % 32 == 0, "32 rows x 4 stages per workgroup");
+  const int hgroups = (stages + 3) / 4;                   // consecutive workgroups sweep one row group's K
+  const long long g = blockIdx.x / hgroups;
+  const int h = (int)(blockIdx.x - g * hgroups);
+  const long long row = g * 32 + (threadIdx.x >> 3);
+  const int pair = threadIdx.x & 7;                       // blocks 2 pair, 2 pair + 1 of the four stages
+  const int stage = h * 4 + (pair >> 1);
   if (stage >= stages) return;
-  const int kg = stage * kbs + (int)(threadIdx.x % kbs);
-  u32x2 c = {0u, 0u};
-  uint32_t sc = 0u;
-  if (row < rows && kg < kb_real) c = quant_linear_block(src + (row * kb_real + kg) * kBlock, r, sc);
+  const int kg = stage * kbs + 2 * (pair & 1);            // first of the two blocks
+  u32x4 c = {0u, 0u, 0u, 0u};
+  uint32_t s2 = 0u;
+  if (row < rows && kg + 1 < kb_real) {                   // both blocks: all four loads issued first
+    const u32x4* p = (const u32x4*)(src + (row * kb_real + kg) * kBlock);
+    const u32x4 a0 = p[0], b0 = p[1], a1 = p[2], b1 = p[3];
+    uint32_t s0, s1;
+    const u32x2 c0 = quant_linear_raw(a0, b0, r, s0);
+    const u32x2 c1 = quant_linear_raw(a1, b1, r, s1);
+    c = u32x4{c0[0], c0[1], c1[0], c1[1]};
+    s2 = (s0 & 0xFFu) | ((s1 & 0xFFu) << 8);
+  } else if (row < rows && kg < kb_real) {                // the row's last block, K / 16 odd
+    uint32_t s0;
+    const u32x2 c0 = quant_linear_block(src + (row * kb_real + kg) * kBlock, r, s0);
+    c[0] = c0[0];
+    c[1] = c0[1];
+    s2 = s0 & 0xFFu;
+  }
   const long long chunk = (row / kLinTileRows) * stages + stage;
-  const int within = (int)(row % kLinTileRows) * kbs + (int)(threadIdx.x % kbs);
-  *(u32x2*)(codes + chunk * (kLinTileRows * kLinStage / 2) + 8 * within) = c;
-  scales[chunk * (kLinTileRows * kbs) + within] = (uint8_t)sc;
+  const int within = (int)(row % kLinTileRows) * kbs + 2 * (pair & 1);
+  *(u32x4*)(codes + chunk * (kLinTileRows * kLinStage / 2) + 8 * within) = c;
+  *(uint16_t*)(scales + chunk * (kLinTileRows * kbs) + within) = (uint16_t)s2;
 }
 
 // ---------------------------------------------------------------- mean -------
@@ -489,9 +511,9 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* sca
   const float r = (float)(1.0 / (double)global_scale);        // RN32(1/g)
   if (tiled) {
     const int stages = (cols + kLinStage - 1) / kLinStage;
-    const long long row_groups = (rows + kLinTileRows - 1) / kLinTileRows * (kLinTileRows / 16);
-    if (row_groups > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(nvfp4_quant_tiled_kernel, dim3((unsigned)row_groups, (unsigned)((stages + 3) / 4)),
+    const long long groups = (rows + kLinTileRows - 1) / kLinTileRows * (kLinTileRows / 32) * ((stages + 3) / 4);
+    if (groups > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(nvfp4_quant_tiled_kernel, dim3((unsigned)groups),
                        dim3(QUANT_THREADS), 0, stream, x, codes, scales, rows, cols / kBlock, stages, r);
     return hipGetLastError();
   }
