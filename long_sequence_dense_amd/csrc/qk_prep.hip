@@ -27,10 +27,13 @@
 //                    (tracked per thread with packed 16-bit min/max);
 //                    otherwise the partial is flagged and recomputed exactly
 //                    by kmean_final.
-//   kmean_final      one wave per (head, channel): adds the exact partials
+//   kmean_final      one wave per (head, channel): adds the partials in fp64
+//                    with every addition checked by TwoSum; when one rounded
+//                    (or a partial was flagged), adds the exact partials
 //                    into 320-bit two's-complement integers (units of
 //                    2^-133), combines them, rounds once to fp64 (nearest,
-//                    ties to even), divides by L in fp64 and rounds to fp32.
+//                    ties to even).  Then divides by L in fp64 and rounds to
+//                    fp32.
 //   quant (K)        as for Q after x = RN32(k - mean).
 // Ablation variants (same section: plain quantization against quantization
 // after the two transforms): without smoothing the mean kernels are skipped
@@ -438,8 +441,21 @@ struct BigSum {
   }
 };
 
-// One wave per (head, channel): each lane adds its share of the partials into
-// its own 320-bit integer, then lane 0 adds the 64 integers (exact).
+// s + e = a + b exactly (Knuth's TwoSum, round to nearest, no overflow): the
+// fp64 addition a + b was exact iff e == 0.
+__device__ __forceinline__ double two_sum(double a, double b, double& e) {
+  const double s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+  return s;
+}
+
+// One wave per (head, channel).  Fast path: the partials are added in fp64
+// (each lane its share, then a butterfly across the wave), every addition
+// checked with TwoSum; if none rounded and no partial was flagged, the fp64
+// result is the exact column sum.  Otherwise: each lane adds its share into
+// its own 320-bit integer, then lane 0 adds the 64 integers (exact).  Both
+// paths round the exact sum once to fp64.
 constexpr int FINAL_THREADS = 64;
 
 __global__ __launch_bounds__(FINAL_THREADS) void kmean_final_kernel(const uint16_t* __restrict__ k,
@@ -450,6 +466,26 @@ __global__ __launch_bounds__(FINAL_THREADS) void kmean_final_kernel(const uint16
   const int h = i / kHeadDim, c = i - h * kHeadDim;
   const int lane = threadIdx.x;
   const double* p = parts + (size_t)i * nparts;
+  {
+    double sum = 0.0;
+    bool exact = true;
+    for (int j = lane; j < nparts; j += FINAL_THREADS) {
+      const double d = p[j];
+      double e;
+      sum = two_sum(sum, d, e);
+      exact = exact && d == d && e == 0.0;
+    }
+#pragma unroll
+    for (int off = FINAL_THREADS / 2; off > 0; off >>= 1) {
+      double e;
+      sum = two_sum(sum, __shfl_xor(sum, off, FINAL_THREADS), e);
+      exact = exact && e == 0.0;
+    }
+    if (__all(exact)) {                          // uniform across the wave
+      if (lane == 0) kmean[i] = (float)((sum == 0.0 ? 0.0 : sum) / (double)L);   // an exact zero sum is +0
+      return;
+    }
+  }
   BigSum acc;
   acc.clear();
   for (int j = lane; j < nparts; j += FINAL_THREADS) {

@@ -226,6 +226,29 @@ def test_prep_special_values_exact(torch):
     check_prep_exact("prep special", got, qk_prep_fp4(q, k))
 
 
+def test_prep_mean_combination_rounds(torch):
+    """Column partials that are each exact but whose fp64 combination rounds:
+    channel 3 of the one head holds 2^22 and 2^-2 on rows 0 and 16 (one
+    partial) and 2^-31 on rows 4 and 8 (two others).  Added pairwise in fp64
+    the two 2^-31 fall on ties and are lost, leaving 2^22 + 2^-2, whose mean
+    over 64 rows is an fp32 tie that rounds down; the exact sum carries 2^-30
+    more and its mean rounds up.  A final reduction that trusted the fp64 sum
+    without checking it would be one fp32 ulp low."""
+    from oracle.nvfp4 import qk_prep_fp4
+    rng = np.random.default_rng(11)
+    H, L = 1, 64
+    q = inputs.f32_to_bf16_bits(rng.standard_normal((H, L, 128)).astype(np.float32))
+    k = np.zeros((H, L, 128), np.uint16)
+    k[0, 0, 3], k[0, 16, 3] = 0x4A80, 0x3E80          # 2^22, 2^-2
+    k[0, 4, 3] = k[0, 8, 3] = 0x3000                   # 2^-31
+    d = {"q": q, "k": k}
+    ref = qk_prep_fp4(q, k)
+    assert ref["k_mean"][0, 3] == np.float32(2.0 ** 16 + 2.0 ** -7)    # the exact sum's mean, rounded once
+    say("case prep mean combination rounds")
+    got = run_prep(torch, d)
+    check_prep_exact("prep mean combination", got, ref)
+
+
 def test_prep_deterministic(torch):
     d = inputs.make_inputs("fp4", H=2, L=2000)
     a = run_prep(torch, d)
