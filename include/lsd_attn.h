@@ -266,8 +266,8 @@ size_t nvfp4_scales_bytes(long long rows, int cols, int layout);
  *             aligned.  Within a row, byte j holds value 2j in its low nibble
  *             and 2j+1 in its high nibble (E2M1: sign bit 3, magnitude index
  *             0..7 for 0, .5, 1, 1.5, 2, 3, 4, 6).
- *   scales  : nvfp4_scales_bytes(rows, cols, layout) bytes, written: one E4M3
- *             code per 16 consecutive values of a row.
+ *   scales  : nvfp4_scales_bytes(rows, cols, layout) bytes, written, 16-byte
+ *             aligned: one E4M3 code per 16 consecutive values of a row.
  *   rows >= 1, cols >= 16 and a multiple of 16, rows * cols / 16 < 2^39
  *   (else LSD_ERR_SHAPE); layout an lsd_nvfp4_layout (else LSD_ERR_FLAGS).
  *   global_scale : g, float32, finite, > 0 and with a finite float32 1/g
@@ -296,7 +296,8 @@ int nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long
  *   y       : [M, N] BF16 bits, row-major, written (round to nearest even).
  *   M >= 1, N >= 1, K >= 16 and a multiple of 16, K <= 2^20 (else
  *   LSD_ERR_SHAPE); the scales must be finite and > 0 (else LSD_ERR_SCALE);
- *   code pointers 16-byte aligned, y 8-byte aligned (else LSD_ERR_ALIGN).
+ *   code and scale pointers 16-byte aligned, y 8-byte aligned (else
+ *   LSD_ERR_ALIGN).
  * Both operands are dequantized exactly on chip (an E2M1 value times an E4M3
  * scale fits FP16 and BF16), their products accumulate in fp32 on the matrix
  * cores, the fp32 sum is multiplied by RN32(g_x * g_w) and rounded to BF16.

@@ -185,7 +185,7 @@ int nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long
   if (rows < 1 || cols < lsd::kBlock || cols % lsd::kBlock) return LSD_ERR_SHAPE;
   if (rows > (1LL << 40) || rows * (cols / lsd::kBlock) >= (1LL << 39)) return LSD_ERR_SHAPE;
   if (!x || !codes || !scales) return LSD_ERR_NULL;
-  if (!aligned16(x) || !aligned16(codes)) return LSD_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return LSD_ERR_ALIGN;
   if (check_scale(global_scale) != LSD_OK || !std::isfinite((float)(1.0 / (double)global_scale)))
     return LSD_ERR_SCALE;
   (void)hipGetLastError();
@@ -199,7 +199,9 @@ int nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, float x_global
   if (layout != LSD_NVFP4_ROWS && layout != LSD_NVFP4_TILED) return LSD_ERR_FLAGS;
   if (M < 1 || N < 1 || K < lsd::kBlock || K % lsd::kBlock || K > (1 << 20)) return LSD_ERR_SHAPE;
   if (!x_codes || !x_scales || !w_codes || !w_scales || !y) return LSD_ERR_NULL;
-  if (!aligned16(x_codes) || !aligned16(w_codes) || ((uintptr_t)y & 7u)) return LSD_ERR_ALIGN;
+  if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      ((uintptr_t)y & 7u))
+    return LSD_ERR_ALIGN;
   if (check_scale(x_global_scale) != LSD_OK || check_scale(w_global_scale) != LSD_OK) return LSD_ERR_SCALE;
   (void)hipGetLastError();
   return launch_status(lsd::launch_nvfp4_linear(x_codes, x_scales, x_global_scale, w_codes, w_scales,

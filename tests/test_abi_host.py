@@ -180,6 +180,7 @@ def test_nvfp4_quantize_argument_errors(lib):
         assert f(A, A, N, 4, 32, 1.0, layout, N) == 1
         assert f(B, A, A, 4, 32, 1.0, layout, N) == 4                   # x misaligned
         assert f(A, B, A, 4, 32, 1.0, layout, N) == 4                   # codes misaligned
+        assert f(A, A, B, 4, 32, 1.0, layout, N) == 4                   # scales misaligned
         assert f(A, A, A, 4, 32, 0.0, layout, N) == 7
         assert f(A, A, A, 4, 32, -2.0, layout, N) == 7
         assert f(A, A, A, 4, 32, float("inf"), layout, N) == 7
@@ -202,6 +203,8 @@ def test_nvfp4_linear_argument_errors(lib):
             assert f(*args, 8, 8, 64, layout, N) == 1, i
         assert f(B, A, 1.0, A, A, 1.0, A, 8, 8, 64, layout, N) == 4     # x codes misaligned
         assert f(A, A, 1.0, B, A, 1.0, A, 8, 8, 64, layout, N) == 4
+        assert f(A, B, 1.0, A, A, 1.0, A, 8, 8, 64, layout, N) == 4     # x scales misaligned
+        assert f(A, A, 1.0, A, B, 1.0, A, 8, 8, 64, layout, N) == 4     # w scales misaligned
         assert f(A, A, 1.0, A, A, 1.0, ctypes.c_void_p(0x100004), 8, 8, 64, layout, N) == 4    # y needs 8 bytes
         assert f(A, A, 0.0, A, A, 1.0, A, 8, 8, 64, layout, N) == 7
         assert f(A, A, 1.0, A, A, float("nan"), A, 8, 8, 64, layout, N) == 7
