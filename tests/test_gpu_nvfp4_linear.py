@@ -106,6 +106,70 @@ def test_quantize_bit_exact(torch, rows, cols, seed, gsel, layout):
     check_codes("x %dx%d" % (rows, cols), c, s, bits, g, layout)
 
 
+def e4m3_value(j):
+    """OCP E4M3 value of the positive code j (1 <= j <= 126), from the bit
+    fields: exponent j >> 3 (bias 7), mantissa j & 7, subnormals m * 2^-9."""
+    e, m = j >> 3, j & 7
+    return 2.0 ** (e - 7) * (1 + m / 8) if e else m * 2.0 ** -9
+
+
+def tie_blocks(seed=9):
+    """One 16-value block per row that puts the quantizer's decisions on and
+    next to every rounding boundary (all of them are BF16 values: each has at
+    most 7 significant bits):
+      - scale boundaries: block max = 6 x the midpoint of neighbouring E4M3
+        values, and the BF16 values just below and above it;
+      - code boundaries: for every scale v (block max 6 v, so the scale is v
+        exactly) the E2M1 midpoints times v, and the BF16 values around them;
+      - saturation: block maxima at, just above and far above 6 x 448.
+    Signs, positions and the filler values are seeded."""
+    rng = np.random.default_rng(seed)
+    to_bits = lambda a: inputs.f32_to_bf16_bits(np.atleast_1d(np.asarray(a, np.float32)))
+    one = lambda x: int(to_bits(x)[0])
+    up = lambda b: b + 1                      # next BF16 magnitude (positive bit patterns)
+    down = lambda b: b - 1
+    rows = []
+
+    def block(amax_bits, others_bits):
+        vals = np.zeros(16, np.uint16)
+        pos = rng.permutation(16)
+        vals[pos[0]] = amax_bits
+        for i, b in enumerate(others_bits[:15]):
+            vals[pos[1 + i]] = b
+        signs = rng.integers(0, 2, 16).astype(np.uint16) << 15
+        rows.append(vals | signs)
+
+    vs = [e4m3_value(j) for j in range(1, 127)]
+    for c in range(0, 126):                   # scale midpoints between codes c and c + 1
+        lo = vs[c - 1] if c else 0.0
+        mid6 = 3.0 * (lo + vs[c])
+        b = one(mid6)
+        assert float(inputs.bf16_bits_to_f32(np.uint16(b))) == mid6
+        for a in (b, down(b), up(b)):
+            filler = to_bits(rng.uniform(0, 1, 15) * float(inputs.bf16_bits_to_f32(np.uint16(a))))
+            block(a, list(filler))
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    for v in vs:                              # code midpoints at every scale
+        amax = one(6.0 * v)
+        ties = [one(t * v) for t in mids]
+        assert all(float(inputs.bf16_bits_to_f32(np.uint16(b))) == t * v for b, t in zip(ties, mids))
+        near = [up(b) for b in ties] + [down(b) for b in ties]
+        block(amax, ties + near[:8])
+        block(amax, near[8:] + [0, 0x8000, one(v / 64)] + list(to_bits(rng.uniform(0, 6 * v, 6))))
+    for amax in (2688.0, 2700.0, 3000.0, 1.0e6):
+        b = one(amax)
+        block(b, list(to_bits([2688.0, 2600.0, 2500.0, 2400.0, 448.0 * 5, 448.0 * 5.5, 1.0, 0.0])))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("layout", [ROWS, TILED])
+def test_quantize_every_rounding_boundary(torch, layout):
+    bits = tie_blocks()
+    say("case quantize rounding boundaries rows=%d layout=%d" % (bits.shape[0], layout))
+    c, s = gpu_quantize(torch, bits, 1.0, layout)
+    check_codes("boundaries", c, s, bits, 1.0, layout)
+
+
 def compare(tag, got, want, bound):
     err = np.abs(got - want)
     ratio = float(np.max(err / (2.0 * bound + 2.0 ** -120)))
