@@ -14,6 +14,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblsd_attn.so")
 HEAD_DIM = 128
+ABI_VERSION = 3         # LSD_ABI_VERSION of include/lsd_attn.h, which SIGNATURES mirrors
 
 STATUS = {
     0: "LSD_OK", 1: "LSD_ERR_NULL", 2: "LSD_ERR_SHAPE", 3: "LSD_ERR_UNSUPPORTED_D",
@@ -71,6 +72,9 @@ def load_library(path=None):
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args
+    if lib.lsd_abi_version() != ABI_VERSION:
+        raise RuntimeError("%s has ABI version %d, this binding expects %d; rebuild it with "
+                           "`python -m long_sequence_dense_amd.build`" % (p, lib.lsd_abi_version(), ABI_VERSION))
     if path is None:
         _lib = lib
     return lib

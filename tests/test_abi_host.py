@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.lsd_abi_version() == 3
+    assert lib.lsd_abi_version() == 3 == binding.ABI_VERSION
+    assert "#define LSD_ABI_VERSION 3\n" in open(HEADER).read()
     for st in range(9):
         assert lib.lsd_status_str(st).decode()
     assert lib.lsd_status_str(99).decode() == "unknown status"
