@@ -348,3 +348,42 @@ def test_fp4qk_full_size_sampled(torch):
     oref, lref = fp4_oracle(d, heads=heads, rows=rows)
     check_attention("fp4qk full-size sampled", o, l, oref, lref, rows=rows, heads=heads)
     assert not torch.isnan(o).any().item()
+
+
+def test_offsets_beyond_2gib(torch):
+    """80 heads of the 15-second FP4 workload: every BF16 tensor is 2.23 GB,
+    so the last heads start past 2^31 bytes.  BF16 attention, the prep (every
+    code, scale and mean of the checked heads) and FP4-QK attention on the
+    first and the last head."""
+    from long_sequence_dense_amd import binding
+    from oracle.attention import attention_fp64
+    from oracle.nvfp4 import dequant_nvfp4, qk_prep_fp4
+    H, L = 80, 109000
+    heads = [0, H - 1]
+    rows = inputs.sample_rows(L, 24)
+    say("case offsets beyond 2 GiB: fp4 structure H=%d L=%d (generate)" % (H, L))
+    d = inputs.make_inputs("fp4", H=H, L=L)
+    assert (H - 1) * L * 128 * 2 > 2 ** 31
+
+    say("  bf16 attention")
+    o, l = run_bf16(torch, d)
+    oref, lref = attention_fp64(f64(d["q"][heads]), f64(d["k"][heads]), f64(d["v"][heads]), d["scale"], rows=rows)
+    check_attention("bf16 H=80 sampled", o, l, oref, lref, rows=rows, heads=heads)
+    assert not torch.isnan(o).any().item()
+    del o, l
+
+    say("  prep + fp4qk attention")
+    prep = run_prep(torch, d)
+    ref = qk_prep_fp4(d["q"][heads], d["k"][heads])
+    check_prep_exact("prep H=80 heads %s" % heads, prep, ref, heads=heads)
+    v = bf16_dev(torch, d["v"])
+    o = torch.full((H, L, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    l = torch.full((H, L), float("nan"), dtype=torch.float32, device="cuda")
+    binding.attn_fwd_fp4qk(prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"],
+                           v, o, l, softmax_scale=d["scale"])
+    torch.cuda.synchronize()
+    qh = dequant_nvfp4(ref["q_codes"], ref["q_scales"])
+    kh = dequant_nvfp4(ref["k_codes"], ref["k_scales"])
+    oref, lref = attention_fp64(qh, kh, f64(d["v"][heads]), d["scale"], rows=rows)
+    check_attention("fp4qk H=80 sampled", o, l, oref, lref, rows=rows, heads=heads)
+    assert not torch.isnan(o).any().item()
