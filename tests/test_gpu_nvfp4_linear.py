@@ -240,9 +240,20 @@ def test_linear_full_size(torch, layout):
     """Full-size projection as the benchmark runs it (tiled) and row-major:
     all weight codes bit exact, sampled token rows' codes bit exact and their
     outputs within the bound."""
+    linear_sampled(torch, layout, FULL_M, FULL_N, FULL_K, "full")
+
+
+@pytest.mark.parametrize("layout", [ROWS, TILED])
+def test_linear_output_beyond_2gib(torch, layout):
+    """A 300,000 x 4096 BF16 output (2.46 GB): output rows past 2^31 bytes,
+    checked as in the full-size case."""
+    assert 300000 * 4096 * 2 > 2 ** 31
+    linear_sampled(torch, layout, 300000, 4096, 1024, "output past 2 GiB")
+
+
+def linear_sampled(torch, layout, M, N, K, tag):
     from long_sequence_dense_amd import binding
-    M, N, K = FULL_M, FULL_N, FULL_K
-    say("case linear full M=%d N=%d K=%d layout=%d (generate)" % (M, N, K, layout))
+    say("case linear %s M=%d N=%d K=%d layout=%d (generate)" % (tag, M, N, K, layout))
     xb = inputs.linear_operand("x", M, K, 7)
     wb = inputs.linear_operand("w", N, K, 8)
     gx, gw = calibrated(xb), calibrated(wb)
