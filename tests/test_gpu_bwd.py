@@ -132,16 +132,27 @@ def test_bwd_full_size(torch):
     """40 heads x 109,000 tokens: dQ on sampled rows of sampled heads against
     the row-local oracle; dK and dV of every key through the sums that softmax
     fixes (sum over keys of dK = 0, of dV = sum over queries of dO)."""
+    bwd_sampled(torch, 40)
+
+
+def test_bwd_beyond_2gib(torch):
+    """The same checks at 80 heads (2.23 GB per BF16 tensor): the last heads'
+    rows lie past 2^31 bytes."""
+    assert 79 * 109000 * 128 * 2 > 2 ** 31
+    bwd_sampled(torch, 80)
+
+
+def bwd_sampled(torch, H):
     from oracle.attention_bwd import attention_bwd_dq_bound_rows_fp64, attention_bwd_dq_rows_fp64
-    c = inputs.CONFIGS["clip15s"]
-    say("case bwd clip15s H=40 L=109000 (generate)")
-    d = inputs.make_inputs("clip15s")
+    c = inputs.CONFIGS["clip15s"].with_shape(H=H)
+    say("case bwd clip15s H=%d L=%d (generate)" % (c.H, c.L))
+    d = inputs.make_inputs(c)
     dob = inputs.make_tensor(c, "do")
     (dq, dk, dv), o = run_bwd(torch, d, dob)
     for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert not torch.isnan(g).any().item(), name
     rows = inputs.sample_rows(c.L, 40)
-    heads = [0, 21, 39]
+    heads = [0, H * 21 // 40, H - 1]
     gq = to_f64(dq[heads][:, rows])
     a = [(f64(d["q"][h][rows]), f64(d["k"][h]), f64(d["v"][h]), f64(dob[h][rows]), d["scale"]) for h in heads]
     rq = np.stack([attention_bwd_dq_rows_fp64(*x) for x in a])
