@@ -225,22 +225,57 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_kernel(const uint16_t* __
   *(uint16_t*)(scales + row * (kHeadDim / kBlock) + part * 2) = (uint16_t)(scode[0] | (scode[1] << 8));
 }
 
-// NVFP4 quantization of the rows of a linear layer's operand: y = RN32(x * r)
-// with r = RN32(1 / g) for the tensor's global scale g, then each block of 16
-// consecutive values of a row is quantized as above (no rotation).
-__device__ __forceinline__ u32x2 quant_linear_raw(u32x4 a, u32x4 b, float r, uint32_t& sc) {
+// NVFP4 quantization of the rows of a linear layer's operand: y = RN32(x / g)
+// for the tensor's global scale g, then each block of 16 consecutive values of
+// a row is quantized as above (no rotation).
+//
+// The quotient is formed as y = RN32(RN64(x * r64)) with r64 = RN64(1 / g);
+// for every BF16 x and float32 g > 0 whose quotient is not in float32's
+// subnormal range, that is exactly RN32(x / g):
+//   * x = X 2^a and g = G 2^b with odd integers X < 2^8 and G < 2^24.  A
+//     rounding boundary of normal float32 values (a midpoint, or the overflow
+//     threshold 2^128 - 2^103) is m = M 2^c with M odd, 2^24 < M < 2^25.
+//     x / g = m would need X = G M > 2^8: impossible.  Otherwise
+//     x / g - m = (X 2^a - G M 2^(b+c)) / (G 2^b), and a > b + c (the two
+//     terms are within a factor of two and X < 2^8 < M), so the numerator is
+//     a nonzero multiple of 2^(b+c): x / g is at least 2^c / G, i.e. more
+//     than 2^-49 |m|, away from m.
+//   * r64 and the product are one fp64 rounding each: the product lies within
+//     (1 + 2^-53)^2 - 1 < 2^-52 of x / g relatively, on the same side of every
+//     boundary, so rounding it to float32 gives the float32 nearest to x / g
+//     (infinite past the overflow threshold).
+// Subnormal quotients (|product| < 2^-126) can sit exactly on a boundary
+// (x = 15 * 2^-133, g = 3 * 2^17 gives 5 * 2^-150); there the fp64 quotient
+// x / g (IEEE division, exact whenever x / g fits in fp64) rounded to float32
+// is used, which is RN32(x / g) by Figueroa's double-rounding theorem
+// (53 >= 2 * 24 + 2).  An infinite y is replaced by +-FLT_MAX: it takes the
+// same scale (448) and the same code (+-6) as +-inf.
+struct GlobalScale {
+  double r;   // RN64(1 / g)
+  double g;
+};
+
+__device__ __forceinline__ float div_global(uint32_t bits, const GlobalScale& gs) {
+  const double x = (double)__uint_as_float(bits);
+  double p = x * gs.r;
+  if (__builtin_fabs(p) < 0x1p-126) p = x / gs.g;
+  const float y = (float)p;
+  return __builtin_fminf(__builtin_fmaxf(y, -3.40282347e38f), 3.40282347e38f);
+}
+
+__device__ __forceinline__ u32x2 quant_linear_raw(u32x4 a, u32x4 b, const GlobalScale& gs, uint32_t& sc) {
   float y[16];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    y[2 * j] = __uint_as_float(a[j] << 16) * r;
-    y[2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u) * r;
-    y[8 + 2 * j] = __uint_as_float(b[j] << 16) * r;
-    y[8 + 2 * j + 1] = __uint_as_float(b[j] & 0xFFFF0000u) * r;
+    y[2 * j] = div_global(a[j] << 16, gs);
+    y[2 * j + 1] = div_global(a[j] & 0xFFFF0000u, gs);
+    y[8 + 2 * j] = div_global(b[j] << 16, gs);
+    y[8 + 2 * j + 1] = div_global(b[j] & 0xFFFF0000u, gs);
   }
   return quant_block16(y, sc);
 }
 
-__device__ __forceinline__ u32x2 quant_linear_block(const uint16_t* src, float r, uint32_t& sc) {
+__device__ __forceinline__ u32x2 quant_linear_block(const uint16_t* src, const GlobalScale& r, uint32_t& sc) {
   const u32x4* p = (const u32x4*)src;
   return quant_linear_raw(p[0], p[1], r, sc);
 }
@@ -250,7 +285,7 @@ __device__ __forceinline__ u32x2 quant_linear_block(const uint16_t* src, float r
 __global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_rows_kernel(const uint16_t* __restrict__ src,
                                                                         uint8_t* __restrict__ codes,
                                                                         uint8_t* __restrict__ scales,
-                                                                        long long nblocks, float r) {
+                                                                        long long nblocks, GlobalScale r) {
   const long long i = (long long)blockIdx.x * QUANT_THREADS + threadIdx.x;
   if (i >= nblocks) return;
   uint32_t sc;
@@ -271,7 +306,7 @@ __global__ __launch_bounds__(QUANT_THREADS) void nvfp4_quant_tiled_kernel(const 
                                                                          uint8_t* __restrict__ codes,
                                                                          uint8_t* __restrict__ scales,
                                                                          long long rows, int kb_real, int stages,
-                                                                         float r) {
+                                                                         GlobalScale r) {
   constexpr int kbs = kLinStage / kBlock;                 // blocks per row per stage
   static_assert(QUANT_THREADS == 32 * 8 && kbs == 4 && kLinTileRows % 32 == 0, "32 rows x 4 stages per workgroup");
   const int hgroups = (stages + 3) / 4;                   // consecutive workgroups sweep one row group's K
@@ -544,7 +579,7 @@ void launch_quant(const uint16_t* src, const float* kmean, uint8_t* codes, uint8
 
 hipError_t launch_nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long rows, int cols,
                                  float global_scale, bool tiled, hipStream_t stream) {
-  const float r = (float)(1.0 / (double)global_scale);        // RN32(1/g)
+  const GlobalScale r = {1.0 / (double)global_scale, (double)global_scale};
   if (tiled) {
     const int stages = (cols + kLinStage - 1) / kLinStage;
     const long long groups = (rows + kLinTileRows - 1) / kLinTileRows * (kLinTileRows / 32) * ((stages + 3) / 4);

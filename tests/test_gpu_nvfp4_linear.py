@@ -170,6 +170,51 @@ def test_quantize_every_rounding_boundary(torch, layout):
     check_codes("boundaries", c, s, bits, 1.0, layout)
 
 
+@pytest.mark.parametrize("layout", [ROWS, TILED])
+def test_quantize_quotient_next_to_decisions(torch, layout):
+    """Blocks whose exact x / g lies next to the rounding boundary beside a
+    code or scale threshold (tests/quotient_cases.py, each with its own odd
+    float32 g): only the correctly rounded quotient RN32(x / g) gives the
+    oracle's codes and scales on all of them."""
+    from quotient_cases import quotient_cases
+    cases = quotient_cases(60)
+    say("case quantize quotient next to decisions: %d blocks, layout=%d" % (len(cases), layout))
+    for i, (bits, g, kind, tau) in enumerate(cases):
+        c, s = gpu_quantize(torch, bits[None], float(g), layout)
+        check_codes("quotient case %d (%s)" % (i, kind), c, s, bits[None], float(g), layout)
+
+
+def test_quantize_overflowing_quotient_saturates(torch):
+    """x / g beyond the float32 range (the largest BF16 values with g < 1):
+    scale 448 and code +-6, as for any value past 6 * 448 * g."""
+    x = np.zeros((2, 32), np.uint16)
+    x[0, :4] = [0x7F7F, 0xFF7F, 0x7F00, 0x3F80]        # +-3.39e38, 1.7e38, 1.0
+    x[1, 16:19] = [0x7F7F, 0x0001, 0x8000]             # and a subnormal and -0 beside it
+    for g in (0.5, float(np.float32(0.9999)), float(np.float32(1e-30))):
+        say("case quantize overflowing quotient g=%r" % g)
+        for layout in (ROWS, TILED):
+            c, s = gpu_quantize(torch, x, g, layout)
+            check_codes("overflow g=%r" % g, c, s, x, g, layout)
+
+
+def test_quantize_subnormal_quotients(torch):
+    """Quotients in float32's subnormal range, among them exact rounding ties
+    (15 * 2^-133 / (3 * 2^17) = 2.5 * 2^-149) and values below half the
+    smallest subnormal: the values of a block scaled so small that its scale
+    is a subnormal E4M3 value or zero."""
+    rng = np.random.default_rng(17)
+    x = np.zeros((3, 32), np.uint16)
+    x[0, :16] = 0x000F                                 # 15 * 2^-133 (BF16 subnormal)
+    x[0, 16:] = rng.integers(1, 0x80, 16)              # BF16 subnormals
+    x[1] = inputs.f32_to_bf16_bits((rng.standard_normal(32) * 1e-38).astype(np.float32))
+    x[2] = rng.integers(0, 0x0300, 32).astype(np.uint16) | (rng.integers(0, 2, 32).astype(np.uint16) << 15)
+    for g in (float(3 * 2 ** 17), float(np.float32(7.77e5)), 1.0):
+        say("case quantize subnormal quotients g=%r" % g)
+        for layout in (ROWS, TILED):
+            c, s = gpu_quantize(torch, x, g, layout)
+            check_codes("subnormal g=%r" % g, c, s, x, g, layout)
+
+
 def compare(tag, got, want, bound):
     err = np.abs(got - want)
     ratio = float(np.max(err / (2.0 * bound + 2.0 ** -120)))

@@ -206,3 +206,27 @@ def test_overflowed_quotient_saturates_like_clipping():
     c, s = lin.quantize(x, np.float32(0.5))
     assert s[0, 0] == 0x7E
     assert c[0, 0] == (0x7 | (0xF << 4)) and c[0, 1] & 0xF == 0x7
+
+
+def test_quotient_cases_decide_codes_by_one_ulp():
+    # The constructed blocks (tests/quotient_cases.py) put x / g next to the
+    # midpoint beside a code or scale threshold: the oracle's correctly
+    # rounded quotient and the multiply by a rounded reciprocal give different
+    # codes or scales on many of them, so bit-exact agreement on these blocks
+    # pins the quotient's rounding.
+    from quotient_cases import quotient_cases
+    from long_sequence_dense_amd import inputs
+    cases = quotient_cases(60)
+    differ = 0
+    for bits, g, kind, tau in cases:
+        x = inputs.bf16_bits_to_f32(bits).astype(np.float64)[None]
+        c, s = lin.quantize(x, g)
+        r = np.float32(1.0 / np.float64(g))
+        alt = (x * np.float64(r)).astype(np.float32)
+        ca, sa = nvfp4._quantize_rows(alt, rotate=False)
+        differ += (not np.array_equal(c, ca)) or (not np.array_equal(s, sa))
+        # the deciding element's x' is the threshold or its float32 neighbour
+        xs = lin.scaled_input(x, g)[0]
+        d = np.abs(np.abs(xs.astype(np.float64)) - float(tau))
+        assert d.min() <= float(np.spacing(np.float32(float(tau)))), (kind, float(tau))
+    assert differ >= len(cases) // 10, differ
