@@ -254,19 +254,25 @@ __device__ __forceinline__ void schedule_qk_half() {
   }
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // Exponentials of the tile against the reference max in use, their BF16
-// operands and the lane's partial sum.
+// operands and the lane's partial sum.  The sum is taken over the BF16-rounded
+// values that P.V multiplies (two per dot instruction, fp32 accumulation), so
+// numerator and denominator carry the same weights: a row whose weight sits on
+// one key returns that key's V row exactly, up to the output's rounding.
 __device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float c, float negm, bf16x8 (&p)[4]) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float lsum = 0.0f;
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) {
     f32x8 pf;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc >> 1][8 * (cc & 1) + i], c, negm));
-      lsum += pf[i];
-    }
+    for (int i = 0; i < 8; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cc >> 1][8 * (cc & 1) + i], c, negm));
     p[cc] = __builtin_convertvector(pf, bf16x8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[cc][2 * j], p[cc][2 * j + 1]}, ones, lsum, false);
   }
   return lsum;
 }
