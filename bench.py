@@ -86,13 +86,15 @@ def stored_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(H, L, d):
+def cpu_baseline(H, L, d, gpu_rows=None):
     """Time the CPU oracle (as it stands) on a bounded sample of the workload
     (about 15 s of CPU work on 16 cores) and extrapolate a full step; returns
-    the cpu_baseline object."""
+    the cpu_baseline object.  ``gpu_rows(name, heads, rows)`` returns the GPU
+    step's outputs (float64) for those rows: the oracle values computed here
+    are then also compared with them (``parity``)."""
     from long_sequence_dense_amd import inputs
     from oracle.attention import attention_fp64
-    from oracle.nvfp4 import qk_prep_fp4
+    from oracle.nvfp4 import dequant_nvfp4, qk_prep_fp4
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -106,7 +108,7 @@ def cpu_baseline(H, L, d):
     v = inputs.make_tensor(cfg, "v", heads)
     f = lambda b: inputs.bf16_bits_to_f32(b).astype(np.float64)
     t0 = time.time()
-    attention_fp64(f(q), f(k), f(v), cfg.scale, rows=rows)
+    oref, _ = attention_fp64(f(q), f(k), f(v), cfg.scale, rows=rows)
     t_attn = time.time() - t0
     attn_rate = len(heads) * len(rows) * 4.0 * L * d / t_attn          # FLOP/s
     fcfg = inputs.CONFIGS["fp4"]
@@ -114,12 +116,12 @@ def cpu_baseline(H, L, d):
     qf = inputs.make_tensor(fcfg, "q", prep_heads)
     kf = inputs.make_tensor(fcfg, "k", prep_heads)
     t0 = time.time()
-    qk_prep_fp4(qf, kf)
+    ref = qk_prep_fp4(qf, kf)
     t_prep = time.time() - t0
     t_prep_head = t_prep / len(prep_heads)
     full_attn_s = attn_flop(H, L, d) / attn_rate
     step_s = 2 * full_attn_s + H * t_prep_head
-    return {
+    out = {
         "value": round(2 * attn_flop(H, L, d) / step_s / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(cores),
@@ -130,6 +132,28 @@ def cpu_baseline(H, L, d):
                    % (len(rows), len(heads), L, t_attn, attn_rate / 1e9, len(prep_heads), t_prep,
                       step_s, H)),
     }
+    if gpu_rows is not None:
+        # Not timed: the same oracle rows against the GPU step's outputs, and
+        # the FP4-QK error as a fraction of the quantization error on head 0:
+        # ||O_gpu - O(same codes)|| / ||O(same codes) - O(exact)||.
+        err = np.abs(gpu_rows("bf16", heads, rows) - oref)
+        frows = inputs.sample_rows(L, 2048, seed=7)
+        qh = dequant_nvfp4(ref["q_codes"][:1], ref["q_scales"][:1])
+        kh = dequant_nvfp4(ref["k_codes"][:1], ref["k_scales"][:1])
+        vf = f(inputs.make_tensor(fcfg, "v", [0]))
+        o_same, _ = attention_fp64(qh, kh, vf, fcfg.scale, rows=frows)
+        o_exact, _ = attention_fp64(f(qf[:1]), f(kf[:1]), vf, fcfg.scale, rows=frows)
+        g5 = gpu_rows("fp4", [0], frows)
+        e5 = np.abs(g5 - o_same)
+        ratio = float(np.linalg.norm(g5 - o_same) / np.linalg.norm(o_same - o_exact))
+        out["parity"] = {
+            "attn_fwd_bf16": {"rows": "%d sampled rows x heads %s" % (len(rows), heads),
+                              "max_abs": float(err.max()), "mean_abs": float(err.mean())},
+            "attn_fwd_fp4qk": {"rows": "%d sampled rows of head 0" % len(frows),
+                               "max_abs": float(e5.max()), "mean_abs": float(e5.mean()),
+                               "error_over_quantization_error": ratio},
+        }
+    return out
 
 
 LIN_M, LIN_N, LIN_K = 109000, 5120, 5120
@@ -189,6 +213,21 @@ def linear_path(torch, binding, stream, dev):
     }
 
 
+def config_path(torch, binding, stream, name, reps):
+    """attn_fwd_bf16 on another configuration of the same method (not in
+    value): seeded inputs generated on the host, one warm-up, ``reps`` timed
+    calls on the launch stream."""
+    cfg, x = gen_inputs(torch, name)
+    o = torch.empty_like(x["q"])
+    t = time_calls(torch, stream, lambda: binding.attn_fwd_bf16(x["q"], x["k"], x["v"], o, None, cfg.scale, stream),
+                   n=reps)
+    fl = attn_flop(cfg.H, cfg.L)
+    tf = fl / (t * 1e-3) / 1e12
+    del x, o
+    return {"ms": round(t, 4), "TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "workload": cfg.desc, "in_value": False}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +240,8 @@ def main():
                     help="skip the extra (not in value) timing of attn_bwd_bf16 and attn_bwd_fp4qk")
     ap.add_argument("--no-linear", action="store_true",
                     help="skip the extra (not in value) timing of the NVFP4 linear layer")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the extra (not in value) BF16 timings of the 24 x 8192 and 40 x 36,480 workloads")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for hardware-counter runs: one %d-byte torch copy (counter calibration), "
                          "then one launch of each kernel on the benchmark workload; no timing" % COPY_PROBE_BYTES)
@@ -309,6 +350,29 @@ def main():
         paths["attn_fwd_fp4qk"] = {"ms": round(t_fp4, 3), "TFLOP/s": round(a4, 1),
                                    "frac_of_peak": round(a4 / PEAK_BF16_TFLOPS, 4),
                                    "mfma_precision": "bf16 (exact dequantization of NVFP4 Q/K)"}
+    if args.only != "bf16":
+        # Extra path, outside the step's value: the fused-Q form of the FP4
+        # path (K-only prep, then attention that quantizes Q in its prologue)
+        # on the same inputs; 1 warm-up + 3 timed calls of each part.
+        log("timing the fused-Q FP4 path (3 calls) ...")
+        kflags = binding.PREP_SMOOTH_K | binding.PREP_ROTATE | binding.PREP_K_ONLY
+        kprep = {key: prep[key] for key in ("k_codes", "k_scales", "k_mean")}
+        t_kp = time_calls(torch, stream, lambda: binding.qk_prep_fp4_ex(None, x5["k"], kflags, kprep, ws, stream))
+        o5f = torch.empty_like(o5)
+        t_fq = time_calls(torch, stream, lambda: binding.attn_fwd_fp4qk_fused_q(
+            x5["q"], kprep["k_codes"], kprep["k_scales"], x5["v"], o5f, None, cfg5.scale, stream))
+        same = bool(torch.equal(o5f.view(torch.int16), o5.view(torch.int16)))
+        kbytes = H * L * (2 * d + d // 2 + d // 16)
+        paths["qk_prep_fp4_k_only"] = {"ms": round(t_kp, 4), "GB/s": round(kbytes / (t_kp * 1e-3) / 1e9, 1),
+                                       "algorithmic_bytes": kbytes,
+                                       "frac_of_peak": round(kbytes / (t_kp * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                       "in_value": False}
+        af = fl / (t_fq * 1e-3) / 1e12
+        paths["attn_fwd_fp4qk_fused_q"] = {"ms": round(t_fq, 3), "TFLOP/s": round(af, 1),
+                                           "frac_of_peak": round(af / PEAK_BF16_TFLOPS, 4),
+                                           "output_bit_identical_to_two_call_path": same,
+                                           "fused_path_ms": round(t_kp + t_fq, 3), "in_value": False}
+        del o5f
     if args.only != "bf16" and not args.no_bwd:
         # Extra path, outside the step and its value: the backward of the BF16
         # path on the same inputs, dO ~ N(0, 1); 1 warm-up + 3 timed calls.
@@ -325,7 +389,7 @@ def main():
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            binding.attn_bwd_bf16(x4["q"], x4["k"], x4["v"], o4, lse, dout, *grads, softmax_scale=cfg4.scale,
+            binding.attn_bwd_bf16(x4["q"], x4["k"], x4["v"], lse, dout, *grads, softmax_scale=cfg4.scale,
                                   workspace=bws, stream=stream)
             b.record(stream)
             b.synchronize()
@@ -336,7 +400,8 @@ def main():
         paths["attn_bwd_bf16"] = {"ms": round(t_bwd, 3), "TFLOP/s": round(bw, 1),
                                   "frac_of_peak": round(bw / PEAK_BF16_TFLOPS, 4),
                                   "flop_convention": "2.5 x forward (5 of the 2HL^2d products); the kernels "
-                                                     "compute 7 (S and dP again for dQ)",
+                                                     "compute 9 (S and dP in the row-statistics sweep, "
+                                                     "again for dK/dV and again for dQ)",
                                   "in_value": False}
         # The training-time FP4 backward on the FP4 path's tensors (the codes
         # of the step's prep, its forward's output and LSE): 1 warm-up + 2 calls.
@@ -345,7 +410,7 @@ def main():
                                lse, cfg5.scale, stream)
         fws = torch.empty(binding.attn_bwd_fp4qk_workspace_bytes(H, L, d), dtype=torch.uint8, device=dev)
         t_fb = time_calls(torch, stream, lambda: binding.attn_bwd_fp4qk(
-            prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], x5["v"], o5, lse, dout, *grads,
+            prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], x5["v"], lse, dout, *grads,
             softmax_scale=cfg5.scale, workspace=fws, stream=stream), n=2)
         fb = 2.5 * fl / (t_fb * 1e-3) / 1e12
         paths["attn_bwd_fp4qk"] = {"ms": round(t_fb, 3), "TFLOP/s": round(fb, 1),
@@ -363,6 +428,10 @@ def main():
         log("timing nvfp4_quantize + nvfp4_linear (3 calls each) ...")
         r = linear_path(torch, binding, stream, dev)
         paths.update(r)
+    if args.only != "bf16" and not args.no_configs:
+        log("timing attn_fwd_bf16 on the mid and clip5s workloads ...")
+        paths["attn_fwd_bf16_mid"] = config_path(torch, binding, stream, "mid", 50)
+        paths["attn_fwd_bf16_clip5s"] = config_path(torch, binding, stream, "clip5s", 10)
     traffic = stored_traffic()
     res = {
         "metric": METRIC,
@@ -389,7 +458,20 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        res["cpu_baseline"] = cpu_baseline(H, L, d)
+        def gpu_rows(name, heads, rows):
+            from long_sequence_dense_amd import inputs
+            t = o4 if name == "bf16" else o5
+            idx_h = torch.tensor(heads, device=dev)
+            idx_r = torch.from_numpy(np.asarray(rows)).to(dev)
+            sel = t.index_select(0, idx_h).index_select(1, idx_r)
+            bits = sel.view(torch.int16).cpu().numpy().view(np.uint16)
+            return inputs.bf16_bits_to_f32(bits).astype(np.float64)
+
+        res["cpu_baseline"] = cpu_baseline(H, L, d, gpu_rows if args.only != "bf16" else None)
+        if "parity" in res["cpu_baseline"]:
+            par = res["cpu_baseline"].pop("parity")
+            for key, val in par.items():
+                res["paths"][key]["parity_vs_oracle"] = val
     print(json.dumps(res), flush=True)
 
 

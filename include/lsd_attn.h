@@ -9,7 +9,8 @@
  *                   and NVFP4 block quantization of Q and K (qk_prep_fp4_ex:
  *                   the same with either transform switched off).
  *   attn_fwd_fp4qk  attention whose scores come from the NVFP4 Q and K;
- *                   probabilities and V stay BF16.
+ *                   probabilities and V stay BF16 (attn_fwd_fp4qk_fused_q:
+ *                   the same with Q quantized inside the attention kernel).
  *   attn_bwd_bf16   gradients of attn_fwd_bf16 with respect to Q, K and V.
  *   attn_bwd_fp4qk  training-time gradients of attn_fwd_fp4qk (straight-
  *                   through quantizer), with respect to the original Q, K, V.
@@ -67,7 +68,7 @@ enum lsd_status {
 };
 
 /* Version of this ABI (the value of LSD_ABI_VERSION the library was built with). */
-#define LSD_ABI_VERSION 3
+#define LSD_ABI_VERSION 4
 int lsd_abi_version(void);
 
 /* Static description of a status code ("ok", "null pointer", ...). */
@@ -127,7 +128,8 @@ int qk_prep_fp4(const uint16_t* q, const uint16_t* k,
 /* Bits of the `flags` argument of qk_prep_fp4_ex. */
 enum lsd_prep_flags {
   LSD_PREP_SMOOTH_K = 1,      /* subtract the per-head mean key before quantizing K */
-  LSD_PREP_ROTATE = 2         /* shared 128-point Hadamard rotation of Q and K      */
+  LSD_PREP_ROTATE = 2,        /* shared 128-point Hadamard rotation of Q and K      */
+  LSD_PREP_K_ONLY = 4         /* prepare K only (Q is quantized by attn_fwd_fp4qk_fused_q) */
 };
 
 /*
@@ -140,6 +142,9 @@ enum lsd_prep_flags {
  *           is written with zeros (the mean that was subtracted).
  *   Without LSD_PREP_ROTATE: no butterfly and no 1/sqrt(128) factor; the
  *           16-channel blocks are consecutive original channels.
+ *   With LSD_PREP_K_ONLY: Q is neither read nor written (q, q_codes and
+ *           q_scales may be NULL); K's outputs are those of the same call
+ *           without it.
  * Everything else (layouts, rounding, codes, errors) is as in qk_prep_fp4.
  * Source: "FP4 attention" (quantizing naively costs accuracy; smoothing K and
  * the Hadamard rotation recover part of it; its per-layer error table).
@@ -170,38 +175,65 @@ int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales,
                    int H, int L, int d, float softmax_scale, void* stream);
 
 /*
+ * attn_fwd_fp4qk_fused_q - attn_fwd_fp4qk with Q's preparation done inside
+ * the attention kernel: each workgroup rotates and quantizes its own query
+ * rows (the arithmetic of qk_prep_fp4, so the same codes) and dequantizes them
+ * in registers; Q's codes never go through memory.
+ *   q   : [H, L, d] BF16 bits (the unquantized queries).
+ *   k_codes, k_scales : K prepared by qk_prep_fp4_ex with LSD_PREP_SMOOTH_K |
+ *             LSD_PREP_ROTATE | LSD_PREP_K_ONLY (or by qk_prep_fp4).
+ *   v, o, lse, softmax_scale, shape limits and errors : as attn_fwd_fp4qk.
+ * Bit-identical to qk_prep_fp4 followed by attn_fwd_fp4qk on the same inputs.
+ * Source: "FP4 attention" (a fused kernel applies the transforms while
+ * quantizing Q and K) and "Faster at BF16" (the prologue work of attention
+ * fused into the kernel).
+ */
+int attn_fwd_fp4qk_fused_q(const uint16_t* q, const uint8_t* k_codes,
+                           const uint8_t* k_scales, const uint16_t* v,
+                           uint16_t* o, float* lse, int H, int L, int d,
+                           float softmax_scale, void* stream);
+
+/*
  * Bytes of device workspace attn_bwd_bf16 needs (0 on a bad shape):
- * 2 * H * L * 4 (one fp32 row statistic pair per query row).
+ * 4 * H * L * 4 (four fp32 statistics per query row).
  */
 size_t attn_bwd_bf16_workspace_bytes(int H, int L, int d);
 
 /*
  * attn_bwd_bf16 - gradients of attn_fwd_bf16 with respect to Q, K and V.
  *   q, k, v : [H, L, d] BF16 bits, the forward's inputs.
- *   o       : [H, L, d] BF16 bits, the forward's output.
- *   lse     : [H, L] float32, the forward's natural-log LSE (required).
+ *   lse     : [H, L] float32, the forward's natural-log LSE (required): only
+ *             the reference shift of the recomputed probabilities, which the
+ *             backward normalizes itself (any value within a few units of
+ *             the row's log-sum-exp gives the same gradients).
  *   dout    : [H, L, d] BF16 bits, the gradient of the loss with respect to o.
  *   dq, dk, dv : [H, L, d] BF16 bits, written (round to nearest even of the
  *             fp32 results).  Must not alias any input.
  *   workspace : device buffer of at least attn_bwd_bf16_workspace_bytes
  *             bytes, 256-byte aligned; contents unspecified on return.
  *   softmax_scale : the sigma of the forward.
- * With P = exp(sigma Q K^T - LSE): dV = P^T dO, dP = dO V^T,
- * D = rowsum(dO * O), dS = P * (dP - D), dQ = sigma dS K, dK = sigma dS^T Q.
- * P and dS are rounded to BF16 for the matrix-core products; sums are fp32.
+ * With P = softmax(sigma Q K^T) row-wise: dV = P^T dO, dP = dO V^T,
+ * D = rowsum(P * dP), dS = P * (dP - D), dQ = sigma dS K, dK = sigma dS^T Q.
+ * A first sweep over the keys forms each row's normalization and D from the
+ * same fp32 scores and dP that the gradient sweeps recompute, so D is a
+ * normalized mean of the row's dP under the same weights (the forward's
+ * output is not needed); D is kept relative to the dP of the row's dominant
+ * key, so rows that put nearly all their weight on one key keep the relative
+ * accuracy of their (nearly zero) dS.  P and dS are rounded to BF16 for the matrix-core
+ * products; sums are fp32.  Nine of the 2 H L^2 d products per call.
  * Deterministic (no atomics).  Same shape limits as attn_fwd_bf16.
  * Source: "NVFP4 QAD" and "FP4 attention" (the model is trained with the
  * deployed attention in the loop); the gradients are those of the forward.
  */
 int attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                  const uint16_t* o, const float* lse, const uint16_t* dout,
+                  const float* lse, const uint16_t* dout,
                   uint16_t* dq, uint16_t* dk, uint16_t* dv,
                   void* workspace, size_t workspace_bytes,
                   int H, int L, int d, float softmax_scale, void* stream);
 
 /*
  * Bytes of device workspace attn_bwd_fp4qk needs (0 on a bad shape):
- * 4 * H * L * d * 2 + 2 * H * L * 4 (dequantized Q, K and their gradients in
+ * 4 * H * L * d * 2 + 4 * H * L * 4 (dequantized Q, K and their gradients in
  * BF16, and the row statistics).
  */
 size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d);
@@ -210,8 +242,9 @@ size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d);
  * attn_bwd_fp4qk - training-time gradients of attn_fwd_fp4qk, with the NVFP4
  * quantizer passed straight through (its gradient taken as the identity).
  *   q_codes, q_scales, k_codes, k_scales : as written by qk_prep_fp4(_ex).
- *   v, o, lse : the forward's V (BF16) and the output and natural-log LSE
- *             written by attn_fwd_fp4qk (lse required).
+ *   v, lse  : the forward's V (BF16) and the natural-log LSE written by
+ *             attn_fwd_fp4qk (required; the reference shift, as for
+ *             attn_bwd_bf16).
  *   dout      : [H, L, d] BF16, the gradient of the loss with respect to o.
  *   dq, dk    : [H, L, d] BF16, written: gradients with respect to the
  *             ORIGINAL Q and K (before smoothing and rotation).
@@ -231,7 +264,7 @@ size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d);
  */
 int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales,
                    const uint8_t* k_codes, const uint8_t* k_scales,
-                   const uint16_t* v, const uint16_t* o, const float* lse,
+                   const uint16_t* v, const float* lse,
                    const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                    void* workspace, size_t workspace_bytes,
                    int H, int L, int d, float softmax_scale, int flags, void* stream);
@@ -270,9 +303,11 @@ size_t nvfp4_scales_bytes(long long rows, int cols, int layout);
  *             aligned: one E4M3 code per 16 consecutive values of a row.
  *   rows >= 1, cols >= 16 and a multiple of 16, rows * cols / 16 < 2^39
  *   (else LSD_ERR_SHAPE); layout an lsd_nvfp4_layout (else LSD_ERR_FLAGS).
- *   global_scale : g, float32, finite, > 0 and with a finite float32 1/g
- *             (else LSD_ERR_SCALE).  The quantizer sees x' = RN32(x * RN32(1/g))
- *             and quantizes each block of 16 as qk_prep_fp4 does (E4M3 scale
+ *   global_scale : g, float32, finite and > 0 (else LSD_ERR_SCALE).  The
+ *             quantizer sees x' = RN32(x / g), the correctly rounded float32
+ *             quotient (a quotient past the float32 range saturates like any
+ *             value beyond 6 * 448), and quantizes each block of 16 as
+ *             qk_prep_fp4 does (E4M3 scale
  *             of amax / 6 rounded to nearest even, then each value divided by
  *             it and rounded to nearest even E2M1, saturating at 6); a code e
  *             with block scale s stands for e * s * g, so g sets the clipping
@@ -294,7 +329,7 @@ int nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long
  *             LSD_ERR_FLAGS); LSD_NVFP4_TILED is the faster one (every load
  *             of the product reads whole cache lines).
  *   y       : [M, N] BF16 bits, row-major, written (round to nearest even).
- *   M >= 1, N >= 1, K >= 16 and a multiple of 16, K <= 2^20 (else
+ *   1 <= M, N <= 2^31 - 256, K >= 16 and a multiple of 16, K <= 2^20 (else
  *   LSD_ERR_SHAPE); the scales must be finite and > 0 (else LSD_ERR_SCALE);
  *   code and scale pointers 16-byte aligned, y 8-byte aligned (else
  *   LSD_ERR_ALIGN).

@@ -14,7 +14,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblsd_attn.so")
 HEAD_DIM = 128
-ABI_VERSION = 3         # LSD_ABI_VERSION of include/lsd_attn.h, which SIGNATURES mirrors
+ABI_VERSION = 4         # LSD_ABI_VERSION of include/lsd_attn.h, which SIGNATURES mirrors
 
 STATUS = {
     0: "LSD_OK", 1: "LSD_ERR_NULL", 2: "LSD_ERR_SHAPE", 3: "LSD_ERR_UNSUPPORTED_D",
@@ -23,6 +23,7 @@ STATUS = {
 }
 PREP_SMOOTH_K = 1       # lsd_prep_flags
 PREP_ROTATE = 2
+PREP_K_ONLY = 4
 NVFP4_ROWS = 0          # lsd_nvfp4_layout
 NVFP4_TILED = 1
 
@@ -39,10 +40,11 @@ SIGNATURES = {
     "qk_prep_fp4": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _P]),
     "qk_prep_fp4_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _P]),
     "attn_fwd_fp4qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
+    "attn_fwd_fp4qk_fused_q": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
     "attn_bwd_bf16_workspace_bytes": (_S, [_I, _I, _I]),
-    "attn_bwd_bf16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _F, _P]),
+    "attn_bwd_bf16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _F, _P]),
     "attn_bwd_fp4qk_workspace_bytes": (_S, [_I, _I, _I]),
-    "attn_bwd_fp4qk": (_I, [_P] * 12 + [_S, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_fp4qk": (_I, [_P] * 11 + [_S, _I, _I, _I, _F, _I, _P]),
     "nvfp4_codes_bytes": (_S, [ctypes.c_longlong, _I, _I]),
     "nvfp4_scales_bytes": (_S, [ctypes.c_longlong, _I, _I]),
     "nvfp4_quantize": (_I, [_P, _P, _P, ctypes.c_longlong, _I, _F, _I, _P]),
@@ -141,24 +143,22 @@ def qk_prep_fp4_workspace_bytes(H, L, d=HEAD_DIM):
     return int(load_library().qk_prep_fp4_workspace_bytes(H, L, d))
 
 
-def _prep_outputs(q, k, out):
+def _prep_outputs(q, k, out, with_q=True):
     import torch
-    H, L, d = q.shape
-    _need(q, "q", _bf16_types(), (H, L, d))
+    H, L, d = k.shape
+    if with_q:
+        _need(q, "q", _bf16_types(), (H, L, d))
     _need(k, "k", _bf16_types(), (H, L, d))
-    dev = q.device
+    dev = k.device
+    sides = ("q", "k") if with_q else ("k",)
     if out is None:
-        out = {
-            "q_codes": torch.empty((H, L, d // 2), dtype=torch.uint8, device=dev),
-            "q_scales": torch.empty((H, L, d // 16), dtype=torch.uint8, device=dev),
-            "k_codes": torch.empty((H, L, d // 2), dtype=torch.uint8, device=dev),
-            "k_scales": torch.empty((H, L, d // 16), dtype=torch.uint8, device=dev),
-            "k_mean": torch.empty((H, d), dtype=torch.float32, device=dev),
-        }
-    for n in ("q_codes", "k_codes"):
-        _need(out[n], n, (torch.uint8,), (H, L, d // 2))
-    for n in ("q_scales", "k_scales"):
-        _need(out[n], n, (torch.uint8,), (H, L, d // 16))
+        out = {"k_mean": torch.empty((H, d), dtype=torch.float32, device=dev)}
+        for x in sides:
+            out[x + "_codes"] = torch.empty((H, L, d // 2), dtype=torch.uint8, device=dev)
+            out[x + "_scales"] = torch.empty((H, L, d // 16), dtype=torch.uint8, device=dev)
+    for x in sides:
+        _need(out[x + "_codes"], x + "_codes", (torch.uint8,), (H, L, d // 2))
+        _need(out[x + "_scales"], x + "_scales", (torch.uint8,), (H, L, d // 16))
     _need(out["k_mean"], "k_mean", (torch.float32,), (H, d))
     return out
 
@@ -183,16 +183,19 @@ def qk_prep_fp4(q, k, out=None, workspace=None, stream=None):
 def qk_prep_fp4_ex(q, k, flags, out=None, workspace=None, stream=None):
     """qk_prep_fp4 with the transforms switched by ``flags`` (PREP_SMOOTH_K |
     PREP_ROTATE = the full method).  Without smoothing no workspace is used and
-    k_mean is written with zeros."""
+    k_mean is written with zeros.  With PREP_K_ONLY only K is prepared (``q``
+    may be None; the result has no q_codes / q_scales)."""
     import torch
-    H, L, d = q.shape
-    out = _prep_outputs(q, k, out)
+    H, L, d = k.shape
+    with_q = not flags & PREP_K_ONLY
+    out = _prep_outputs(q, k, out, with_q)
     if workspace is None:
         need = qk_prep_fp4_workspace_bytes(H, L, d) if flags & PREP_SMOOTH_K else 0
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device) if need else None
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load_library().qk_prep_fp4_ex(
-        _ptr(q), _ptr(k), _ptr(out["q_codes"]), _ptr(out["q_scales"]), _ptr(out["k_codes"]),
+        _ptr(q if with_q else None), _ptr(k), _ptr(out.get("q_codes")), _ptr(out.get("q_scales")),
+        _ptr(out["k_codes"]),
         _ptr(out["k_scales"]), _ptr(out["k_mean"]), _ptr(workspace), nbytes, H, L, d, int(flags),
         _stream(stream))
     _check("qk_prep_fp4_ex", st)
@@ -221,16 +224,38 @@ def attn_fwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o=None, lse=None,
     return o
 
 
+def attn_fwd_fp4qk_fused_q(q, k_codes, k_scales, v, o=None, lse=None, softmax_scale=None, stream=None):
+    """attn_fwd_fp4qk with Q ([H, L, 128] BF16) rotated and quantized inside
+    the attention kernel; K as prepared by qk_prep_fp4_ex(..., PREP_K_ONLY |
+    PREP_SMOOTH_K | PREP_ROTATE)."""
+    import torch
+    H, L, d = v.shape
+    for n, t in (("q", q), ("v", v)):
+        _need(t, n, _bf16_types(), (H, L, d))
+    _need(k_codes, "k_codes", (torch.uint8,), (H, L, d // 2))
+    _need(k_scales, "k_scales", (torch.uint8,), (H, L, d // 16))
+    if o is None:
+        o = torch.empty((H, L, d), dtype=torch.bfloat16, device=v.device)
+    _need(o, "o", _bf16_types(), (H, L, d))
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), (H, L))
+    scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    st = load_library().attn_fwd_fp4qk_fused_q(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v), _ptr(o), _ptr(lse),
+                                               H, L, d, scale, _stream(stream))
+    _check("attn_fwd_fp4qk_fused_q", st)
+    return o
+
+
 def attn_bwd_bf16_workspace_bytes(H, L, d=HEAD_DIM):
     return int(load_library().attn_bwd_bf16_workspace_bytes(H, L, d))
 
 
-def attn_bwd_bf16(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, softmax_scale=None,
+def attn_bwd_bf16(q, k, v, lse, dout, dq=None, dk=None, dv=None, softmax_scale=None,
                   workspace=None, stream=None):
-    """Gradients (dq, dk, dv) of attn_fwd_bf16; o and lse are its outputs."""
+    """Gradients (dq, dk, dv) of attn_fwd_bf16; lse is its LSE output."""
     import torch
     H, L, d = q.shape
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+    for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need(t, n, _bf16_types(), (H, L, d))
     _need(lse, "lse", (torch.float32,), (H, L))
     outs = []
@@ -243,7 +268,7 @@ def attn_bwd_bf16(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, softmax_scal
         workspace = torch.empty(attn_bwd_bf16_workspace_bytes(H, L, d), dtype=torch.uint8, device=q.device)
     scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
     st = load_library().attn_bwd_bf16(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), H, L, d, scale, _stream(stream))
     _check("attn_bwd_bf16", st)
     return tuple(outs)
@@ -253,13 +278,13 @@ def attn_bwd_fp4qk_workspace_bytes(H, L, d=HEAD_DIM):
     return int(load_library().attn_bwd_fp4qk_workspace_bytes(H, L, d))
 
 
-def attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, dout, dq=None, dk=None, dv=None,
+def attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, lse, dout, dq=None, dk=None, dv=None,
                    softmax_scale=None, flags=PREP_SMOOTH_K | PREP_ROTATE, workspace=None, stream=None):
     """Straight-through gradients (dq, dk, dv) of attn_fwd_fp4qk with respect
-    to the original Q, K and V; o and lse are the FP4-QK forward's outputs."""
+    to the original Q, K and V; lse is the FP4-QK forward's LSE output."""
     import torch
     H, L, d = v.shape
-    for n, t in (("v", v), ("o", o), ("dout", dout)):
+    for n, t in (("v", v), ("dout", dout)):
         _need(t, n, _bf16_types(), (H, L, d))
     for n, t in (("q_codes", q_codes), ("k_codes", k_codes)):
         _need(t, n, (torch.uint8,), (H, L, d // 2))
@@ -276,7 +301,7 @@ def attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, dout, dq=Non
         workspace = torch.empty(attn_bwd_fp4qk_workspace_bytes(H, L, d), dtype=torch.uint8, device=v.device)
     scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
     st = load_library().attn_bwd_fp4qk(
-        _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+        _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v), _ptr(lse), _ptr(dout),
         _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(workspace), workspace.numel() * workspace.element_size(),
         H, L, d, scale, int(flags), _stream(stream))
     _check("attn_bwd_fp4qk", st)

@@ -76,9 +76,11 @@ int qk_prep_fp4_ex(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8
                    size_t workspace_bytes, int H, int L, int d, int flags, void* stream) {
   int st = check_shape(H, L, d);
   if (st != LSD_OK) return st;
-  if (flags & ~(LSD_PREP_SMOOTH_K | LSD_PREP_ROTATE)) return LSD_ERR_FLAGS;
+  if (flags & ~(LSD_PREP_SMOOTH_K | LSD_PREP_ROTATE | LSD_PREP_K_ONLY)) return LSD_ERR_FLAGS;
   const bool smooth = (flags & LSD_PREP_SMOOTH_K) != 0;
-  if (!q || !k || !q_codes || !q_scales || !k_codes || !k_scales || (smooth && !k_mean)) return LSD_ERR_NULL;
+  const bool with_q = (flags & LSD_PREP_K_ONLY) == 0;
+  if (!k || !k_codes || !k_scales || (smooth && !k_mean)) return LSD_ERR_NULL;
+  if (with_q && (!q || !q_codes || !q_scales)) return LSD_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_codes) || !aligned16(q_scales) ||
       !aligned16(k_codes) || !aligned16(k_scales) || !aligned16(k_mean))
     return LSD_ERR_ALIGN;
@@ -87,7 +89,8 @@ int qk_prep_fp4_ex(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8
     return LSD_ERR_WORKSPACE;
   (void)hipGetLastError();
   return launch_status(lsd::launch_qk_prep(q, k, q_codes, q_scales, k_codes, k_scales, k_mean, workspace,
-                                           H, L, smooth, (flags & LSD_PREP_ROTATE) != 0, (hipStream_t)stream));
+                                           H, L, smooth, (flags & LSD_PREP_ROTATE) != 0, with_q,
+                                           (hipStream_t)stream));
 }
 
 int qk_prep_fp4(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8_t* q_scales,
@@ -114,26 +117,41 @@ int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
                                               softmax_scale * kLog2e, (hipStream_t)stream));
 }
 
+int attn_fwd_fp4qk_fused_q(const uint16_t* q, const uint8_t* k_codes, const uint8_t* k_scales, const uint16_t* v,
+                           uint16_t* o, float* lse, int H, int L, int d, float softmax_scale, void* stream) {
+  int st = check_shape(H, L, d);
+  if (st != LSD_OK) return st;
+  if ((st = check_attn_len(L)) != LSD_OK) return st;
+  if (!q || !k_codes || !k_scales || !v || !o) return LSD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(k_scales) || !aligned16(v) || !aligned16(o))
+    return LSD_ERR_ALIGN;
+  if (lse && ((uintptr_t)lse & 3u)) return LSD_ERR_ALIGN;
+  if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_attn_fp4qk_fused_q(q, k_codes, k_scales, v, o, lse, H, L,
+                                                      softmax_scale * kLog2e, (hipStream_t)stream));
+}
+
 size_t attn_bwd_bf16_workspace_bytes(int H, int L, int d) {
   if (check_shape(H, L, d) != LSD_OK) return 0;
   return lsd::attn_bwd_workspace_bytes(H, L);
 }
 
-int attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o, const float* lse,
+int attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
                   const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
                   size_t workspace_bytes, int H, int L, int d, float softmax_scale, void* stream) {
   int st = check_shape(H, L, d);
   if (st != LSD_OK) return st;
   if ((st = check_attn_len(L)) != LSD_OK) return st;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return LSD_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+  if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv) return LSD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
     return LSD_ERR_ALIGN;
   if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lsd::attn_bwd_workspace_bytes(H, L))
     return LSD_ERR_WORKSPACE;
   (void)hipGetLastError();
-  return launch_status(lsd::launch_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, H, L, softmax_scale,
+  return launch_status(lsd::launch_attn_bwd(q, k, v, lse, dout, dq, dk, dv, workspace, H, L, softmax_scale,
                                             (hipStream_t)stream));
 }
 
@@ -143,24 +161,24 @@ size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d) {
 }
 
 int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
-                   const uint8_t* k_scales, const uint16_t* v, const uint16_t* o, const float* lse,
+                   const uint8_t* k_scales, const uint16_t* v, const float* lse,
                    const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
                    size_t workspace_bytes, int H, int L, int d, float softmax_scale, int flags, void* stream) {
   int st = check_shape(H, L, d);
   if (st != LSD_OK) return st;
   if ((st = check_attn_len(L)) != LSD_OK) return st;
   if (flags & ~(LSD_PREP_SMOOTH_K | LSD_PREP_ROTATE)) return LSD_ERR_FLAGS;
-  if (!q_codes || !q_scales || !k_codes || !k_scales || !v || !o || !lse || !dout || !dq || !dk || !dv)
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v || !lse || !dout || !dq || !dk || !dv)
     return LSD_ERR_NULL;
   if (!aligned16(q_codes) || !aligned16(q_scales) || !aligned16(k_codes) || !aligned16(k_scales) ||
-      !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       ((uintptr_t)lse & 3u))
     return LSD_ERR_ALIGN;
   if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lsd::attn_bwd_fp4qk_workspace_bytes(H, L))
     return LSD_ERR_WORKSPACE;
   (void)hipGetLastError();
-  return launch_status(lsd::launch_attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, dout, dq, dk, dv,
+  return launch_status(lsd::launch_attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, lse, dout, dq, dk, dv,
                                                   workspace, H, L, softmax_scale, (flags & LSD_PREP_ROTATE) != 0,
                                                   (hipStream_t)stream));
 }
@@ -186,8 +204,7 @@ int nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long
   if (rows > (1LL << 40) || rows * (cols / lsd::kBlock) >= (1LL << 39)) return LSD_ERR_SHAPE;
   if (!x || !codes || !scales) return LSD_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return LSD_ERR_ALIGN;
-  if (check_scale(global_scale) != LSD_OK || !std::isfinite((float)(1.0 / (double)global_scale)))
-    return LSD_ERR_SCALE;
+  if (check_scale(global_scale) != LSD_OK) return LSD_ERR_SCALE;
   (void)hipGetLastError();
   return launch_status(lsd::launch_nvfp4_quantize(x, codes, scales, rows, cols, global_scale,
                                                   layout == LSD_NVFP4_TILED, (hipStream_t)stream));
@@ -197,7 +214,9 @@ int nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, float x_global
                  const uint8_t* w_codes, const uint8_t* w_scales, float w_global_scale,
                  uint16_t* y, int M, int N, int K, int layout, void* stream) {
   if (layout != LSD_NVFP4_ROWS && layout != LSD_NVFP4_TILED) return LSD_ERR_FLAGS;
-  if (M < 1 || N < 1 || K < lsd::kBlock || K % lsd::kBlock || K > (1 << 20)) return LSD_ERR_SHAPE;
+  // tile counts are formed as (M + 255) / 256 in 32-bit arithmetic
+  if (M < 1 || N < 1 || M > INT_MAX - 255 || N > INT_MAX - 255) return LSD_ERR_SHAPE;
+  if (K < lsd::kBlock || K % lsd::kBlock || K > (1 << 20)) return LSD_ERR_SHAPE;
   if (!x_codes || !x_scales || !w_codes || !w_scales || !y) return LSD_ERR_NULL;
   if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
       ((uintptr_t)y & 7u))

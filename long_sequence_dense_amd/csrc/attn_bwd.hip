@@ -4,34 +4,50 @@
 // "Pika H3 Flex in FastVideo: 7x Faster, and Near Real Time in 4-bit",
 // section "Faster at BF16"), needed to train through attention as the
 // distillation of section "NVFP4 QAD" does.  With S = sigma Q K^T,
-// P = exp(S - LSE) (LSE saved by the forward), dO the gradient of O:
-//   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,  dS = P * (dP - D),
+// P = softmax(S) row-wise, dO the gradient of O:
+//   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
 //   dQ = sigma dS K,  dK = sigma dS^T Q.
 //
+// The backward recomputes the probabilities and normalizes them itself: the
+// forward's LSE serves only as a reference shift m_i (any value near the row's
+// log-sum-exp keeps exp2 in range), and a first sweep over the keys forms
+// l_i = sum_j exp2(s_ij c - m_i) and D_i = sum_j p_ij dP_ij / l_i from the
+// same fp32 scores and dP the gradient sweeps use.  D is then a normalized
+// weighted mean of the row's dP values under the backward's own weights, so
+// dP_ij - D_i is formed without cancellation against an independently rounded
+// output.  D is also kept relative to the dP of the row's dominant key (the
+// one key with a probability above 1/2, if there is one): the sweeps form
+// (dP_ij - dP_ref) - (D_i - dP_ref), which is exactly -(D_i - dP_ref) at that
+// key, so on rows where one key holds nearly all the weight (dS almost zero)
+// the gradient keeps its relative accuracy instead of an fp32 rounding of
+// dP_ij - D_i.
+//
 // Three launches, deterministic (no atomics):
-//   bwd_rowdot  D_i = dO_i . O_i in fp32 (BF16 products are exact in fp32)
-//               and LSE_i * log2(e), into the workspace.
+//   bwd_dq<stats>  the forward's layout: one wave per 32 queries, eight waves
+//               per workgroup; Q and dO of its rows in registers, 32-key tiles
+//               of K and V through LDS; S^T = K Q^T, dP^T = V dO^T on the
+//               32x32x16 BF16 MFMA; per row m = LSE log2(e), 1 / l, dP_ref
+//               and D - dP_ref into the workspace.
 //   bwd_dkdv    one wave per 32 keys (eight waves, two per SIMD, per
 //               workgroup of 256 keys): K of its keys stays in registers and
 //               the workgroup's V rows in LDS, both read as MFMA B operands;
 //               32-query tiles of Q, dO and their row statistics stream
 //               through LDS (double-buffered, copied by LDS-DMA loads so that
 //               no registers hold the next tile).  Per tile: S and dP on
-//               the 32x32x16 BF16 MFMA with the query tile as the A operand
-//               (rows = queries, columns = this wave's keys), P and dS on the
-//               VALU, then dV^T += dO^T P and dK^T += Q^T dS with the
+//               the MFMA with the query tile as the A operand (rows = queries,
+//               columns = this wave's keys), P = exp2(S c - m) / l and dS on
+//               the VALU, then dV^T += dO^T P and dK^T += Q^T dS with the
 //               transposed query tiles read by ds_read_b64_tr_b16 as the A
 //               operand and P, dS taken from the accumulators as the B operand
 //               (the accumulator layout is the operand layout up to a fixed
 //               permutation of the query index, which the transpose reads
 //               reproduce).
-//   bwd_dq      the forward's layout: one wave per 32 queries, eight waves
-//               per workgroup; Q and dO of its rows in registers, 32-key
-//               tiles of K and V through LDS.  S^T = K Q^T, dP^T = V dO^T,
-//               dS^T on the VALU, dQ^T += K^T dS^T.
+//   bwd_dq<grad> the stats sweep's layout again: dS^T on the VALU,
+//               dQ^T += K^T dS^T.
 // P and dS are rounded to BF16 for their MFMAs; all sums are fp32.  Rows past
-// L are zero-filled by the buffer loads: their keys add nothing, and their
-// queries meet only zero operands (bwd_dq gives them an infinite LSE).
+// L are zero-filled by the buffer loads: their keys are masked out of the
+// row sums and add nothing to dQ (zero K rows), and their queries meet only
+// zero operands (the dQ sweeps give them weight zero).
 #include "lsd_internal.h"
 #include "device_common.h"
 
@@ -153,37 +169,6 @@ __device__ __forceinline__ int xcd_logical(int bid, int nblk) {
   return xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
 }
 
-// ----------------------------------------------------------------- rowdot --
-
-constexpr int ROWDOT_THREADS = 256;            // 16 lanes per row, 16 rows per workgroup
-
-__global__ __launch_bounds__(ROWDOT_THREADS) void bwd_rowdot_kernel(const uint16_t* __restrict__ o,
-                                                                   const uint16_t* __restrict__ dout,
-                                                                   const float* __restrict__ lse,
-                                                                   float* __restrict__ dsum,
-                                                                   float* __restrict__ lse2, long long nrows) {
-  const int tid = threadIdx.x;
-  const long long row = (long long)blockIdx.x * (ROWDOT_THREADS / 16) + (tid >> 4);
-  const int part = tid & 15;                    // channels 8 * part .. +7
-  float acc = 0.0f;
-  if (row < nrows) {
-    const u32x4 a = *(const u32x4*)(o + row * kHeadDim + 8 * part);
-    const u32x4 b = *(const u32x4*)(dout + row * kHeadDim + 8 * part);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = __builtin_fmaf(__uint_as_float(a[j] << 16), __uint_as_float(b[j] << 16), acc);
-      acc = __builtin_fmaf(__uint_as_float(a[j] & 0xFFFF0000u), __uint_as_float(b[j] & 0xFFFF0000u), acc);
-    }
-  }
-  // sum over the 16 lanes of the row
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m, 16);
-  if (row < nrows && part == 0) {
-    dsum[row] = acc;
-    lse2[row] = lse[row] * kLog2eF;
-  }
-}
-
 // ------------------------------------------------------------------- dK dV --
 
 constexpr int DKDV_WAVES = 8;
@@ -196,7 +181,9 @@ struct DkdvParams {
   const uint16_t* v;
   const uint16_t* dout;
   const float* dsum;
-  const float* lse2;
+  const float* m2;
+  const float* invl;
+  const float* dref;
   uint16_t* dk;
   uint16_t* dv;
   int L;
@@ -209,8 +196,10 @@ constexpr int VKS = kHeadDim + 8;       // row stride (bf16) of the stationary V
 struct DkdvSmem {
   uint16_t q[2][TILE];
   uint16_t dout[2][TILE];
-  float lse2[2][TR];
+  float m2[2][TR];
+  float invl[2][TR];
   float dsum[2][TR];
+  float dref[2][TR];
   uint16_t v[DKDV_KEYS * VKS];          // the workgroup's V rows, read as B operands
 };
 
@@ -228,8 +217,10 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
   const size_t head_bytes = (size_t)L * kHeadDim * 2;
   const Rsrc rq = make_rsrc(p.q + head_row0 * kHeadDim, (uint32_t)head_bytes);
   const Rsrc rdo = make_rsrc(p.dout + head_row0 * kHeadDim, (uint32_t)head_bytes);
-  const Rsrc rl = make_rsrc(p.lse2 + head_row0, (uint32_t)L * 4);
+  const Rsrc rm = make_rsrc(p.m2 + head_row0, (uint32_t)L * 4);
+  const Rsrc ri = make_rsrc(p.invl + head_row0, (uint32_t)L * 4);
   const Rsrc rd = make_rsrc(p.dsum + head_row0, (uint32_t)L * 4);
+  const Rsrc rr = make_rsrc(p.dref + head_row0, (uint32_t)L * 4);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // This wave's 32 keys: K and V rows as B operands (8 chunks of 16 channels).
@@ -261,10 +252,9 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
   }
 
   // Query tile q0 into LDS buffer buf: each wave copies 4 rows of Q and of
-  // dO (one row per instruction), waves 0 and 1 the 32 LSE2 and D values.
-  // Rows past L arrive as zeros: their Q and dO rows are zero, so their
-  // probabilities (exp2(0 - 0) = 1) meet only zero operands below and their
-  // dS is zero.
+  // dO (one row per instruction), waves 0 to 3 the 32 values of m, D - dP_ref,
+  // 1 / l and dP_ref.  Rows past L arrive as zeros: their Q and dO rows are zero and
+  // their 1 / l is zero, so their probabilities and dS are zero.
   auto stage = [&](int q0, int buf) {
 #pragma unroll
     for (int i = 0; i < TR / DKDV_WAVES; ++i) {
@@ -273,8 +263,10 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
       dma_dword(rq, sm.q[buf] + r * TS, voff);
       dma_dword(rdo, sm.dout[buf] + r * TS, voff);
     }
-    if (wave_u == 0 && ln.lane < TR) dma_dword(rl, sm.lse2[buf], 4 * (q0 + ln.lane));
+    if (wave_u == 0 && ln.lane < TR) dma_dword(rm, sm.m2[buf], 4 * (q0 + ln.lane));
     if (wave_u == 1 && ln.lane < TR) dma_dword(rd, sm.dsum[buf], 4 * (q0 + ln.lane));
+    if (wave_u == 2 && ln.lane < TR) dma_dword(ri, sm.invl[buf], 4 * (q0 + ln.lane));
+    if (wave_u == 3 && ln.lane < TR) dma_dword(rr, sm.dref[buf], 4 * (q0 + ln.lane));
   };
 
   const int ntiles = (L + TR - 1) / TR;
@@ -296,19 +288,21 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
     for (int kk = 0; kk < 8; ++kk)
       dp = mfma(row_operand(dt, ln.lane_row, kk), __builtin_bit_cast(bf16x8, *(const u16x8*)(sm.v + v_lane + 16 * kk)),
                 dp);
-    // P = exp2(S c - LSE2) and dS = P (dP - D); accumulator element i is
+    // P = exp2(S c - m) / l and dS = P (dP - D); accumulator element i is
     // query row 8 * (i / 4) + 4 * hf + i % 4 of the tile.
     f32x8 pf[2], df[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 l4 = *(const f32x4*)(&sm.lse2[buf][8 * g + 4 * ln.hf]);
+      const f32x4 m4 = *(const f32x4*)(&sm.m2[buf][8 * g + 4 * ln.hf]);
+      const f32x4 i4 = *(const f32x4*)(&sm.invl[buf][8 * g + 4 * ln.hf]);
       const f32x4 d4 = *(const f32x4*)(&sm.dsum[buf][8 * g + 4 * ln.hf]);
+      const f32x4 r4 = *(const f32x4*)(&sm.dref[buf][8 * g + 4 * ln.hf]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * g + j;
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -l4[j]));
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m4[j])) * i4[j];
         pf[i >> 3][i & 7] = pv;
-        df[i >> 3][i & 7] = pv * (dp[i] - d4[j]);
+        df[i >> 3][i & 7] = pv * ((dp[i] - r4[j]) - d4[j]);
       }
     }
     bf16x8 pb[2], dsb[2];
@@ -364,8 +358,11 @@ struct DqParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* dsum;
-  const float* lse2;
+  const float* lse;                             // the forward's LSE (natural log): the reference shift
+  float* dsum;                                  // per row: D - dP_ref, m = LSE log2(e), 1 / l, dP_ref
+  float* m2;                                    // (written by STATS)
+  float* invl;
+  float* dref;
   uint16_t* dq;
   int L;
   int n_qtiles;
@@ -378,6 +375,17 @@ struct DqSmem {
   uint16_t v[2][TILE];
 };
 
+// STATS: the first sweep, per row l = sum_j p_j with p_j = exp2(s_j c - m)
+// and n = sum_j p_j (dP_j - dP_ref) over the keys j < L, stored as m, 1 / l,
+// dP_ref and n / l = D - dP_ref.  dP_ref is the dP of the key whose p exceeds
+// 1/2 (m is the row's log-sum-exp, so p is its probability up to the LSE's
+// rounding; a later such key replaces an earlier one), 0 if there is none;
+// when it changes, n is moved to the new reference exactly as
+// n += l (dP_old - dP_new).  Otherwise the gradient sweep: P = p / l,
+// dS = P ((dP - dP_ref) - (D - dP_ref)), dQ^T += K^T dS^T.  Both sweeps compute
+// S^T and dP^T with the same instructions in the same order, so their fp32
+// values are the same.
+template <bool STATS>
 __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
   __shared__ __attribute__((aligned(16))) DqSmem sm;
   const int tid = threadIdx.x;
@@ -393,7 +401,8 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
   const __amdgpu_buffer_rsrc_t rk = rsrc(p.k + head_row0 * kHeadDim, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = rsrc(p.v + head_row0 * kHeadDim, head_bytes);
 
-  // This wave's 32 query rows: Q and dO as B operands, LSE2 and D per lane.
+  // This wave's 32 query rows: Q and dO as B operands, the row's statistics
+  // per lane.
   const int qrow = qt * DQ_ROWS + wave * 32 + ln.l32;
   const bool qvalid = qrow < L;
   bf16x8 qreg[8], doreg[8];
@@ -407,8 +416,17 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
       doreg[kk] = __builtin_bit_cast(bf16x8, qvalid ? *(const u16x8*)(dp + 16 * kk) : (u16x8)0);
     }
   }
-  const float lse2 = qvalid ? p.lse2[head_row0 + qrow] : __builtin_inff();
-  const float dsum = qvalid ? p.dsum[head_row0 + qrow] : 0.0f;
+  // Rows past L: m = +inf, 1 / l = 0, so every weight is zero.
+  float m, invl = 0.0f, dsum = 0.0f, dref = 0.0f;
+  if constexpr (STATS) {
+    m = qvalid ? p.lse[head_row0 + qrow] * kLog2eF : __builtin_inff();
+  } else {
+    m = qvalid ? p.m2[head_row0 + qrow] : __builtin_inff();
+    invl = qvalid ? p.invl[head_row0 + qrow] : 0.0f;
+    dsum = qvalid ? p.dsum[head_row0 + qrow] : 0.0f;
+    dref = qvalid ? p.dref[head_row0 + qrow] : 0.0f;
+  }
+  float lsum = 0.0f, nsum = 0.0f, pref = 0.0f;
   f32x16 dqacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) dqacc[db] = (f32x16)0.0f;
@@ -434,26 +452,58 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
     const uint16_t* kt = sm.k[buf];
     const uint16_t* vt = sm.v[buf];
     // S^T = K Q^T and dP^T = V dO^T: rows = keys of the tile, columns = this
-    // wave's queries.  Keys past L are zero rows: they add nothing below.
+    // wave's queries; accumulator element i is key 8 * (i / 4) + 4 * hf + i % 4
+    // of the tile.  Keys past L are zero rows.
     f32x16 s = (f32x16)0.0f, dp = (f32x16)0.0f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) s = mfma(row_operand(kt, ln.lane_row, kk), qreg[kk], s);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) dp = mfma(row_operand(vt, ln.lane_row, kk), doreg[kk], dp);
-    f32x8 df[2];
+    if constexpr (STATS) {
+      const int kv0 = t * TR;
+      const bool ragged = kv0 + TR > L;
+      float pv[16], pmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -lse2));
-      df[i >> 3][i & 7] = pv * (dp[i] - dsum);
+      for (int i = 0; i < 16; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m));
+        if (ragged && kv0 + 8 * (i >> 2) + 4 * ln.hf + (i & 3) >= L) pv[i] = 0.0f;
+        pmax = __builtin_fmaxf(pmax, pv[i]);
+      }
+      if (__builtin_expect(pmax > 0.5f, 0)) {     // a dominant key in this lane's part of the tile
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (pv[i] > 0.5f) {
+            nsum = __builtin_fmaf(lsum, dref - dp[i], nsum);
+            dref = dp[i];
+            pref = pv[i];
+          } else {
+            nsum = __builtin_fmaf(pv[i], dp[i] - dref, nsum);
+          }
+          lsum += pv[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          nsum = __builtin_fmaf(pv[i], dp[i] - dref, nsum);
+          lsum += pv[i];
+        }
+      }
+    } else {
+      f32x8 df[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m)) * invl;
+        df[i >> 3][i & 7] = pv * ((dp[i] - dref) - dsum);
+      }
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) dsb[cc] = __builtin_convertvector(df[cc], bf16x8);
+      // dQ^T += K^T dS^T (keys past L: zero K rows add nothing)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dqacc[db] = mfma(tr_operand(kt, ln.lane_tr, cc, db), dsb[cc], dqacc[db]);
     }
-    bf16x8 dsb[2];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) dsb[cc] = __builtin_convertvector(df[cc], bf16x8);
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) dqacc[db] = mfma(tr_operand(kt, ln.lane_tr, cc, db), dsb[cc], dqacc[db]);
 
     if (more) {
       store_rows(sm.k[buf ^ 1], tid, sk);
@@ -462,7 +512,24 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
     __syncthreads();
   }
 
-  if (qvalid) {
+  if constexpr (STATS) {
+    // The two lane halves hold the same query's two key halves.  The half
+    // whose reference key has the larger p keeps its reference; the other
+    // half's n is moved onto it.
+    const float l2 = __shfl_xor(lsum, 32), n2 = __shfl_xor(nsum, 32);
+    const float r2 = __shfl_xor(dref, 32), p2 = __shfl_xor(pref, 32);
+    const bool mine = pref > p2 || (pref == p2 && ln.hf == 0);     // the same choice in both halves
+    const float rc = mine ? dref : r2;
+    const float nc = mine ? __builtin_fmaf(l2, r2 - rc, n2) + nsum : __builtin_fmaf(lsum, dref - rc, nsum) + n2;
+    const float lt = lsum + l2;
+    if (qvalid && ln.hf == 0) {
+      const float il = 1.0f / lt;
+      p.m2[head_row0 + qrow] = m;
+      p.invl[head_row0 + qrow] = il;
+      p.dsum[head_row0 + qrow] = nc * il;
+      p.dref[head_row0 + qrow] = rc;
+    }
+  } else if (qvalid) {
     uint16_t* row = p.dq + (head_row0 + qrow) * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -561,40 +628,41 @@ __global__ __launch_bounds__(ROT_THREADS) void rotate_rows_kernel(const uint16_t
 
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(int H, int L) { return (size_t)2 * H * (size_t)L * sizeof(float); }
+size_t attn_bwd_workspace_bytes(int H, int L) { return (size_t)4 * H * (size_t)L * sizeof(float); }
 
 size_t attn_bwd_fp4qk_workspace_bytes(int H, int L) {
   return (size_t)4 * H * (size_t)L * kHeadDim * 2 + attn_bwd_workspace_bytes(H, L);
 }
 
-hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
-                           const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                           void* ws, int H, int L, float scale, hipStream_t stream) {
+hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
+                           const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, int H, int L,
+                           float scale, hipStream_t stream) {
   const long long nrows = (long long)H * L;
   float* dsum = (float*)ws;
-  float* lse2 = dsum + nrows;
-  const unsigned rblocks = (unsigned)((nrows + (ROWDOT_THREADS / 16) - 1) / (ROWDOT_THREADS / 16));
-  hipLaunchKernelGGL(bwd_rowdot_kernel, dim3(rblocks), dim3(ROWDOT_THREADS), 0, stream, o, dout, lse, dsum, lse2,
-                     nrows);
+  float* m2 = dsum + nrows;
+  float* invl = m2 + nrows;
+  float* dref = invl + nrows;
+
+  DqParams b = {};
+  b.q = q; b.k = k; b.v = v; b.dout = dout; b.lse = lse; b.dsum = dsum; b.m2 = m2; b.invl = invl; b.dref = dref; b.dq = dq;
+  b.L = L; b.n_qtiles = (L + DQ_ROWS - 1) / DQ_ROWS; b.c = scale * kLog2eF; b.scale = scale;
+  const long long nq = (long long)b.n_qtiles * H;
+  if (nq > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)nq), dim3(DQ_THREADS), 0, stream, b);
 
   DkdvParams a = {};
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.dsum = dsum; a.lse2 = lse2; a.dk = dk; a.dv = dv;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.dsum = dsum; a.m2 = m2; a.invl = invl; a.dref = dref; a.dk = dk; a.dv = dv;
   a.L = L; a.n_ktiles = (L + DKDV_KEYS - 1) / DKDV_KEYS; a.c = scale * kLog2eF; a.scale = scale;
   const long long nk = (long long)a.n_ktiles * H;
   if (nk > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)nk), dim3(DKDV_THREADS), 0, stream, a);
 
-  DqParams b = {};
-  b.q = q; b.k = k; b.v = v; b.dout = dout; b.dsum = dsum; b.lse2 = lse2; b.dq = dq;
-  b.L = L; b.n_qtiles = (L + DQ_ROWS - 1) / DQ_ROWS; b.c = scale * kLog2eF; b.scale = scale;
-  const long long nq = (long long)b.n_qtiles * H;
-  if (nq > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)nq), dim3(DQ_THREADS), 0, stream, b);
+  hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)nq), dim3(DQ_THREADS), 0, stream, b);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                                 const uint16_t* v, const uint16_t* o, const float* lse, const uint16_t* dout,
+                                 const uint16_t* v, const float* lse, const uint16_t* dout,
                                  uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, int H, int L, float scale,
                                  bool rotate, hipStream_t stream) {
   const long long nrows = (long long)H * L;
@@ -608,7 +676,7 @@ hipError_t launch_attn_bwd_fp4qk(const uint8_t* qc, const uint8_t* qs, const uin
   const unsigned db = (unsigned)((nblocks + DEQ_THREADS - 1) / DEQ_THREADS);
   hipLaunchKernelGGL(fp4_dequant_kernel, dim3(db), dim3(DEQ_THREADS), 0, stream, qc, qs, qh, nblocks);
   hipLaunchKernelGGL(fp4_dequant_kernel, dim3(db), dim3(DEQ_THREADS), 0, stream, kc, ks, kh, nblocks);
-  hipError_t e = launch_attn_bwd(qh, kh, v, o, lse, dout, rotate ? dqh : dq, rotate ? dkh : dk, dv, stats, H, L,
+  hipError_t e = launch_attn_bwd(qh, kh, v, lse, dout, rotate ? dqh : dq, rotate ? dkh : dk, dv, stats, H, L,
                                  scale, stream);
   if (e != hipSuccess) return e;
   if (rotate) {

@@ -39,9 +39,13 @@
 //     K/V tiles at about the same time.
 //   * The FP4-QK variant dequantizes each K tile (E2M1 x E4M3, exact in BF16)
 //     into the same LDS layout, and its Q rows once, then runs the same
-//     pipeline on BF16 MFMA.
+//     pipeline on BF16 MFMA.  Its fused-Q form takes Q in BF16 and applies
+//     the prep's rotation and quantizer to each wave's rows in the prologue
+//     (the same fp32 operations in the same order, so the same codes), then
+//     dequantizes them in registers: Q's codes never go through memory.
 #include "lsd_internal.h"
 #include "device_common.h"
+#include "nvfp4_quant.h"
 
 namespace lsd {
 namespace {
@@ -346,7 +350,76 @@ __device__ __forceinline__ void step(Smem& sm, WaveState& st, const Ctx& cx, int
   for (int cc = 0; cc < 4; ++cc) st.p_prev[cc] = p_cur[cc];
 }
 
-template <bool FP4>
+// Q of this lane's query row through the prep's transform and quantizer,
+// dequantized exactly: the Sylvester butterfly in fp32 (stage s pairs channel
+// i with i + 2^s as (x_i + x_j, x_i - x_j), stages in order 0..6), times
+// RN32(1/sqrt(128)), then per 16-channel block the E4M3 scale and E2M1 codes
+// of the prep.  Lane (row, hf) holds channels 16 kk + 8 hf + j (kk, j = 0..7):
+// channel bits 0-2 are j, bit 3 is hf (the partner lane, lane ^ 32), bits 4-6
+// are kk.  Each block is split over the lane pair; its maximum is exchanged.
+__device__ __forceinline__ void quant_dequant_q(const uint16_t* qp, bool valid, int hf, bf16x8 (&qreg)[8]) {
+#pragma clang fp contract(off)
+  float x[8][8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const u16x8 t = valid ? *(const u16x8*)(qp + 16 * kk) : (u16x8)0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[kk][j] = bf16_bits_to_f32(t[j]);
+  }
+#pragma unroll
+  for (int st = 0; st < 3; ++st) {                 // stages 0-2: within j
+    const int hs = 1 << st;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if ((j & hs) == 0) {
+          const float a = x[kk][j], b = x[kk][j + hs];
+          x[kk][j] = a + b;
+          x[kk][j + hs] = a - b;
+        }
+  }
+  // stage 3 across the lane pair: the lane with bit 3 clear forms x_i + x_j,
+  // its partner x_i - x_j, each one rounded operation fma(own, +-1, partner)
+  const float k3 = hf ? -1.0f : 1.0f;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[kk][j] = __builtin_fmaf(x[kk][j], k3, __shfl_xor(x[kk][j], 32));
+#pragma unroll
+  for (int st = 0; st < 3; ++st) {                 // stages 4-6: within kk
+    const int hs = 1 << st;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      if ((kk & hs) == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float a = x[kk][j], b = x[kk + hs][j];
+          x[kk][j] = a + b;
+          x[kk + hs][j] = a - b;
+        }
+      }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[kk][j] = x[kk][j] * kHadamardScale;
+      am = __builtin_fmaxf(am, __builtin_fabsf(x[kk][j]));
+    }
+    am = __builtin_fmaxf(am, __shfl_xor(am, 32));
+    const uint32_t sc = e4m3_scale_code(am);
+    const float s = e4m3_pos(sc);
+    const float rinv = scale_reciprocal(sc, s);
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = div_scale(x[kk][j], s, rinv);
+    qreg[kk] = __builtin_bit_cast(bf16x8, dequant8(e2m1_pack8(t), s));
+  }
+}
+
+template <bool FP4, bool QUANT_Q>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
 
@@ -395,6 +468,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
       u16x8 t = qvalid ? *(const u16x8*)(qp + 16 * kk) : (u16x8)0;
       st.qreg[kk] = __builtin_bit_cast(bf16x8, t);
     }
+  } else if constexpr (QUANT_Q) {
+    quant_dequant_q(p.q + (head_row0 + (size_t)(qvalid ? qrow : 0)) * kHeadDim + 8 * hf, qvalid, hf, st.qreg);
   } else {
     const size_t r = head_row0 + (size_t)(qvalid ? qrow : 0);
     const uint8_t* cp = p.qc + r * (kHeadDim / 2);
@@ -473,13 +548,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
   }
 }
 
-hipError_t launch(const AttnParams& prm, bool fp4, int H, hipStream_t stream) {
+hipError_t launch(const AttnParams& prm, bool fp4, bool quant_q, int H, hipStream_t stream) {
   const long long nblk = (long long)prm.n_qtiles * H;
   if (nblk <= 0 || nblk > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  if (fp4)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, prm);
+  if (quant_q)
+    hipLaunchKernelGGL((attn_fwd_kernel<true, true>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, prm);
+  else if (fp4)
+    hipLaunchKernelGGL((attn_fwd_kernel<true, false>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, prm);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, prm);
+    hipLaunchKernelGGL((attn_fwd_kernel<false, false>), dim3((unsigned)nblk), dim3(NTHREADS), 0, stream, prm);
   return hipGetLastError();
 }
 
@@ -490,7 +567,7 @@ hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t
   AttnParams prm = {};
   prm.q = q; prm.k = k; prm.v = v; prm.o = o; prm.lse = lse;
   prm.L = L; prm.n_qtiles = (L + BR - 1) / BR; prm.scale_log2 = scale_log2;
-  return launch(prm, false, H, stream);
+  return launch(prm, false, false, H, stream);
 }
 
 hipError_t launch_attn_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
@@ -499,7 +576,15 @@ hipError_t launch_attn_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t
   AttnParams prm = {};
   prm.qc = qc; prm.qs = qs; prm.kc = kc; prm.ks = ks; prm.v = v; prm.o = o; prm.lse = lse;
   prm.L = L; prm.n_qtiles = (L + BR - 1) / BR; prm.scale_log2 = scale_log2;
-  return launch(prm, true, H, stream);
+  return launch(prm, true, false, H, stream);
+}
+
+hipError_t launch_attn_fp4qk_fused_q(const uint16_t* q, const uint8_t* kc, const uint8_t* ks, const uint16_t* v,
+                                     uint16_t* o, float* lse, int H, int L, float scale_log2, hipStream_t stream) {
+  AttnParams prm = {};
+  prm.q = q; prm.kc = kc; prm.ks = ks; prm.v = v; prm.o = o; prm.lse = lse;
+  prm.L = L; prm.n_qtiles = (L + BR - 1) / BR; prm.scale_log2 = scale_log2;
+  return launch(prm, true, true, H, stream);
 }
 
 }  // namespace lsd

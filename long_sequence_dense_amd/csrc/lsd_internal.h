@@ -17,15 +17,18 @@ hipError_t launch_attn_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t
                              const uint8_t* ks, const uint16_t* v, uint16_t* o, float* lse,
                              int H, int L, float scale_log2, hipStream_t stream);
 
+hipError_t launch_attn_fp4qk_fused_q(const uint16_t* q, const uint8_t* kc, const uint8_t* ks, const uint16_t* v,
+                                     uint16_t* o, float* lse, int H, int L, float scale_log2, hipStream_t stream);
+
 // attention backward (attn_bwd.hip)
 size_t attn_bwd_workspace_bytes(int H, int L);
-hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
-                           const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                           void* ws, int H, int L, float scale, hipStream_t stream);
+hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
+                           const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, int H, int L,
+                           float scale, hipStream_t stream);
 
 size_t attn_bwd_fp4qk_workspace_bytes(int H, int L);
 hipError_t launch_attn_bwd_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                                 const uint16_t* v, const uint16_t* o, const float* lse, const uint16_t* dout,
+                                 const uint16_t* v, const float* lse, const uint16_t* dout,
                                  uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, int H, int L, float scale,
                                  bool rotate, hipStream_t stream);
 
@@ -33,7 +36,7 @@ hipError_t launch_attn_bwd_fp4qk(const uint8_t* qc, const uint8_t* qs, const uin
 size_t prep_workspace_bytes(int H, int L);
 hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uint8_t* qs,
                           uint8_t* kc, uint8_t* ks, float* kmean, void* ws, int H, int L,
-                          bool smooth, bool rotate, hipStream_t stream);
+                          bool smooth, bool rotate, bool with_q, hipStream_t stream);
 
 // NVFP4 W4A4 linear layer (qk_prep.hip: quantizer, nvfp4_gemm.hip: product).
 // Tiled code layout: rows in tiles of kLinTileRows, K in stages of kLinStage

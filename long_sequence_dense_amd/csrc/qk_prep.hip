@@ -41,6 +41,7 @@
 // 1/sqrt(128) factor are skipped and each block is 16 consecutive channels.
 #include "lsd_internal.h"
 #include "device_common.h"
+#include "nvfp4_quant.h"
 
 namespace lsd {
 namespace {
@@ -54,7 +55,6 @@ constexpr int MEAN_PER_THREAD = MEAN_ROWS / MEAN_SLOTS;   // values summed by on
 // certified exact: MEAN_PER_THREAD * 2^(span + 8) <= 2^53.
 constexpr int kMeanSpan = 45 - __builtin_ctz(MEAN_PER_THREAD);
 static_assert((MEAN_PER_THREAD & (MEAN_PER_THREAD - 1)) == 0, "rows per thread must be a power of two");
-constexpr float kHadamardScale = 0x1.6a09e6p-4f;   // RN32(1/sqrt(128)), bits 0x3DB504F3
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -62,78 +62,12 @@ int mean_chunks(int L) { return (L + MEAN_ROWS - 1) / MEAN_ROWS; }
 
 // ---------------------------------------------------------------- quantizer --
 
-__device__ __forceinline__ float e4m3_pos(uint32_t j) {            // value of code j, 0 <= j <= 126
-  const uint32_t e = j >> 3, m = j & 7;
-  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * (1.0f / 512.0f);
-}
-
-// Nearest E4M3 code to amax/6 (ties to the even code, saturating at 448).
-// Candidate: round r = RN(amax * RN(1/6)) (within a few units in the last
-// place of amax/6) to 3 mantissa bits; then settle it exactly against the
-// values of max|y| where the nearest scale changes, 6 * (v_{c-1} + v_c) / 2 and
-// 6 * (v_c + v_{c+1}) / 2 (at most 7 significant bits: exact in fp32), which
-// moves it by at most one.
-__device__ __forceinline__ uint32_t e4m3_scale_code(float amax) {
-  const float r = amax * 0x1.555556p-3f;
-  uint32_t c;
-  if (!(r < 448.0f)) {
-    c = 0x7Eu;
-  } else if (r >= 0x1p-6f) {
-    const uint32_t u = __float_as_uint(r);
-    c = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
-    c = c > 0x7Eu ? 0x7Eu : c;
-  } else {
-    c = (uint32_t)__builtin_rintf(r * 512.0f);
-  }
-  const float v = e4m3_pos(c);
-  const float hi = c < 0x7Eu ? 3.0f * (v + e4m3_pos(c + 1)) : __builtin_inff();
-  const float lo = c > 0u ? 3.0f * (e4m3_pos(c - 1) + v) : -1.0f;
-  if (amax > hi || (amax == hi && (c & 1u))) return c + 1;          // a tie goes to the even neighbour
-  if (amax < lo || (amax == lo && (c & 1u))) return c - 1;
-  return c;
-}
-
 // Partner value across the lane quad: lane ^ 1 and lane ^ 2.
 __device__ __forceinline__ float dpp_xor1(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 __device__ __forceinline__ float dpp_xor2(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
-}
-
-// One 16-value block: its E4M3 scale code (nearest to max|y| / 6) and the
-// packed E2M1 codes of y / scale (value j in nibble j, low nibble first).
-__device__ __forceinline__ u32x2 quant_block16(float* y, uint32_t& scode) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2)
-    amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(y[i]), __builtin_fabsf(y[i + 1])));
-  const uint32_t sc = e4m3_scale_code(amax);
-  scode = sc;
-  const float s = e4m3_pos(sc);
-  const float rinv = sc ? (float)(1.0 / (double)s) : 0.0f;     // RN32(1/s)
-  // t = RN32(y / s): Markstein's correction from q0 = RN(y * RN(1/s)); the
-  // remainder fma(q0, s, -y) is exact.  Written so that t keeps the sign of
-  // y also when y is a signed zero, and t = +-0 when s = 0 (rinv = 0).
-  float t[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float q0 = y[i] * rinv;
-    const float rr = __builtin_fmaf(q0, s, -y[i]);
-    t[i] = __builtin_fmaf(-rr, rinv, q0);
-  }
-  // E2M1 with round-to-nearest-even and saturation (unit scale).
-  u32x2 w;
-#pragma unroll
-  for (int d = 0; d < 2; ++d) {
-    uint32_t acc = 0u;
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, t[8 * d + 0], t[8 * d + 1], 1.0f, 0);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, t[8 * d + 2], t[8 * d + 3], 1.0f, 1);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, t[8 * d + 4], t[8 * d + 5], 1.0f, 2);
-    acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, t[8 * d + 6], t[8 * d + 7], 1.0f, 3);
-    w[d] = acc;
-  }
-  return w;
 }
 
 // Four lanes per 128-channel row, 32 consecutive channels per lane.  grid:
@@ -255,23 +189,42 @@ struct GlobalScale {
   double g;
 };
 
-__device__ __forceinline__ float div_global(uint32_t bits, const GlobalScale& gs) {
-  const double x = (double)__uint_as_float(bits);
-  double p = x * gs.r;
-  if (__builtin_fabs(p) < 0x1p-126) p = x / gs.g;
-  const float y = (float)p;
+__device__ __forceinline__ float clamp_finite(float y) {
   return __builtin_fminf(__builtin_fmaxf(y, -3.40282347e38f), 3.40282347e38f);
 }
 
+// Sixteen quotients of one block.  The rare subnormal ones are redone with the
+// division behind one branch for the whole block, so the common path stays a
+// multiply and two conversions per value.
+__device__ __forceinline__ void div_global16(const float* x, const GlobalScale& gs, float* y) {
+  bool rare = false;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const double p = (double)x[i] * gs.r;
+    rare = rare || (p != 0.0 && __builtin_fabs(p) < 0x1p-126);
+    y[i] = (float)p;
+  }
+  if (__builtin_expect(rare, 0)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const double p = (double)x[i] * gs.r;
+      if (p != 0.0 && __builtin_fabs(p) < 0x1p-126) y[i] = (float)((double)x[i] / gs.g);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = clamp_finite(y[i]);
+}
+
 __device__ __forceinline__ u32x2 quant_linear_raw(u32x4 a, u32x4 b, const GlobalScale& gs, uint32_t& sc) {
-  float y[16];
+  float x[16], y[16];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    y[2 * j] = div_global(a[j] << 16, gs);
-    y[2 * j + 1] = div_global(a[j] & 0xFFFF0000u, gs);
-    y[8 + 2 * j] = div_global(b[j] << 16, gs);
-    y[8 + 2 * j + 1] = div_global(b[j] & 0xFFFF0000u, gs);
+    x[2 * j] = __uint_as_float(a[j] << 16);
+    x[2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u);
+    x[8 + 2 * j] = __uint_as_float(b[j] << 16);
+    x[8 + 2 * j + 1] = __uint_as_float(b[j] & 0xFFFF0000u);
   }
+  div_global16(x, gs, y);
   return quant_block16(y, sc);
 }
 
@@ -602,9 +555,11 @@ size_t prep_workspace_bytes(int H, int L) {
 
 hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uint8_t* qs, uint8_t* kc,
                           uint8_t* ks, float* kmean, void* ws, int H, int L, bool smooth, bool rotate,
-                          hipStream_t stream) {
-  if (rotate) launch_quant<false, true>(q, nullptr, qc, qs, H, L, stream);
-  else launch_quant<false, false>(q, nullptr, qc, qs, H, L, stream);
+                          bool with_q, hipStream_t stream) {
+  if (with_q) {
+    if (rotate) launch_quant<false, true>(q, nullptr, qc, qs, H, L, stream);
+    else launch_quant<false, false>(q, nullptr, qc, qs, H, L, stream);
+  }
   if (smooth) {
     double* parts = (double*)ws;
     const int nchunks = mean_chunks(L);

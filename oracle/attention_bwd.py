@@ -23,6 +23,9 @@ Pins (tests/test_oracle_attention_bwd.py): central finite differences of
 keys: dQ = 0); the exact sums implied by softmax (sum over keys of dK is zero,
 sum over keys of dV is the sum over queries of dO); covariance under a shared
 orthonormal rotation of Q and K; planted mistakes fail the finite differences.
+The row-local and key-subset forms (for sampled checks at full size) equal
+the full gradient's rows, and the row statistics equal the forward oracle's
+LSE and the row sums of dO * O.
 
 Inputs are float64 arrays (the exact values of BF16 inputs); numpy's fp64
 matmul is the only library primitive used.
@@ -73,6 +76,51 @@ def attention_bwd_dq_rows_fp64(q_rows, k, v, do_rows, scale):
     return float(scale) * (ds @ k)
 
 
+def attention_row_stats_fp64(q_rows, k, v, do_rows, scale):
+    """Per-query statistics of one head for a set of query rows (row-local):
+    LSE_i = m_i + ln sum_j exp(s_ij - m_i) and D_i = sum_j P_ij dP_ij, which is
+    sum_c dO_ic O_ic.  q_rows, do_rows [n, d]; k, v [L, d].  Returns (lse [n],
+    dsum [n])."""
+    q_rows, k, v, do_rows = (np.asarray(t, dtype=np.float64) for t in (q_rows, k, v, do_rows))
+    s = (q_rows @ k.T) * float(scale)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    dp = do_rows @ v.T
+    return m[:, 0] + np.log(l[:, 0]), (p * dp).sum(axis=1)
+
+
+def attention_bwd_keys_fp64(q, k, v, do, scale, keys, lse, dsum, block=4096):
+    """dK and dV of one head for a set of key rows: every query contributes,
+    through P_ij = exp(s_ij - LSE_i) and dS_ij = P_ij (dP_ij - D_i) with the
+    per-query LSE and D of ``attention_row_stats_fp64`` over all L queries.
+    q, k, v, do [L, d]; keys: index array; lse, dsum [L].  Queries are taken
+    ``block`` at a time only to bound memory.  Returns (dk [n, d], dv [n, d])."""
+    q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
+    keys = np.asarray(keys, dtype=np.int64)
+    kj, vj = k[keys], v[keys]
+    dk = np.zeros((keys.size, k.shape[1]))
+    dv = np.zeros((keys.size, v.shape[1]))
+    sc = float(scale)
+    for b0 in range(0, q.shape[0], block):
+        sl = slice(b0, min(q.shape[0], b0 + block))
+        p = np.exp((q[sl] @ kj.T) * sc - np.asarray(lse, dtype=np.float64)[sl, None])
+        ds = p * (do[sl] @ vj.T - np.asarray(dsum, dtype=np.float64)[sl, None])
+        dv += p.T @ do[sl]
+        dk += sc * (ds.T @ q[sl])
+    return dk, dv
+
+
+def hadamard_orthonormal(d):
+    """H_d / sqrt(d): Sylvester's Hadamard matrix (natural order), scaled to
+    be orthonormal; symmetric and its own inverse."""
+    h = np.array([[1.0]])
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h / np.sqrt(d)
+
+
 def fp4qk_bwd_ste_fp64(q_codes, q_scales, k_codes, k_scales, v, do, scale, rotate=True, smooth=True):
     """Training-time gradients of FP4-QK attention with the quantizer passed
     straight through (the gradient of a rounding step taken as the identity).
@@ -96,10 +144,7 @@ def fp4qk_bwd_ste_fp64(q_codes, q_scales, k_codes, k_scales, v, do, scale, rotat
     dqh, dkh, dv = attention_bwd_fp64(qh, kh, v, do, scale)
     d = qh.shape[-1]
     if rotate:
-        h = np.array([[1.0]])
-        while h.shape[0] < d:
-            h = np.block([[h, h], [h, -h]])
-        r = h / np.sqrt(d)
+        r = hadamard_orthonormal(d)
         dq = dqh @ r.T
         dk = dkh @ r.T
     else:
@@ -107,75 +152,3 @@ def fp4qk_bwd_ste_fp64(q_codes, q_scales, k_codes, k_scales, v, do, scale, rotat
     if smooth:
         dk = dk - dk.mean(axis=1, keepdims=True)
     return dq, dk, dv
-
-
-BF16_UNIT = 2.0 ** -8      # unit roundoff of BF16 (8 significant bits, round to nearest)
-
-
-def attention_bwd_bound_fp64(q, k, v, do, scale, u=BF16_UNIT, block=1024):
-    """Elementwise bounds on the error of a BF16 backward (used as test
-    tolerances, derived from that arithmetic, not a property of the method).
-
-    Model, with u the BF16 unit roundoff: D is formed from the output O rounded
-    to BF16 (|D err| <= u sum_c |dO_ic O_ic|), P and dS enter the products
-    rounded to BF16 (u each),
-    the products are exact and their fp32 sums add a sqrt(L) 2^-24 relative
-    term, and the outputs are rounded to BF16 (u).  With a_i = sum_c |dO_ic
-    O_ic| and t = u + sqrt(L) 2^-24:
-        B_dQ = sigma (u a_i (P |K|)_ic + t (|dS| |K|)_ic) + u |dQ_ic|
-        B_dK = sigma (u (P^T (a |Q|))_jc + t (|dS|^T |Q|)_jc) + u |dK_jc|
-        B_dV = t (P^T |dO|)_jc + u |dV_jc|
-    Returns (bq, bk, bv) float64 [H, L, d].
-    """
-    q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
-    H, L, d = q.shape
-    t = u + np.sqrt(L) * 2.0 ** -24
-    bq = np.empty_like(q)
-    bk = np.zeros_like(k)
-    bv = np.zeros_like(v)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
-    sc = float(scale)
-    for h in range(H):
-        ak, aq = np.abs(k[h]), np.abs(q[h])
-        for b0 in range(0, L, block):
-            sl = slice(b0, min(L, b0 + block))
-            p = _softmax_rows((q[h, sl] @ k[h].T) * sc)
-            o = p @ v[h]
-            dp = do[h, sl] @ v[h].T
-            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-            a = np.abs(do[h, sl] * o).sum(axis=1, keepdims=True)
-            dq = sc * (ds @ k[h])
-            bq[h, sl] = sc * (u * a * (p @ ak) + t * (np.abs(ds) @ ak)) + u * np.abs(dq)
-            bk[h] += sc * (u * (p.T @ (a * aq[sl])) + t * (np.abs(ds).T @ aq[sl]))
-            bv[h] += t * (p.T @ np.abs(do[h, sl]))
-            dk[h] += sc * (ds.T @ q[h, sl])
-            dv[h] += p.T @ do[h, sl]
-    return bq, bk + u * np.abs(dk), bv + u * np.abs(dv)
-
-
-def attention_bwd_dq_bound_rows_fp64(q_rows, k, v, do_rows, scale, u=BF16_UNIT):
-    """B_dQ of attention_bwd_bound_fp64 for a set of query rows of one head."""
-    q_rows, k, v, do_rows = (np.asarray(t, dtype=np.float64) for t in (q_rows, k, v, do_rows))
-    L = k.shape[0]
-    t = u + np.sqrt(L) * 2.0 ** -24
-    sc = float(scale)
-    p = _softmax_rows((q_rows @ k.T) * sc)
-    o = p @ v
-    dp = do_rows @ v.T
-    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-    a = np.abs(do_rows * o).sum(axis=1, keepdims=True)
-    ak = np.abs(k)
-    return sc * (u * a * (p @ ak) + t * (np.abs(ds) @ ak)) + u * np.abs(sc * (ds @ k))
-
-
-def rotate_bound(b, g, u=BF16_UNIT, omitted=None):
-    """Bound after rotating back by R = H / sqrt(d): |err(x R)| <= (sum of the
-    row's bounds) / sqrt(d) + u |x R| for the result rounded again to BF16.
-    ``b``: bounds in the rotated basis, ``g``: the rotated-back gradient;
-    ``omitted``: the magnitude of a term the kernel leaves out (the mean-key
-    Jacobian's term, zero in exact arithmetic), added to the bound."""
-    b = np.asarray(b, dtype=np.float64)
-    d = b.shape[-1]
-    out = b.sum(axis=-1, keepdims=True) / np.sqrt(d) + u * np.abs(np.asarray(g, dtype=np.float64))
-    return out if omitted is None else out + np.abs(omitted)

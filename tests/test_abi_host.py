@@ -38,8 +38,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.lsd_abi_version() == 3 == binding.ABI_VERSION
-    assert "#define LSD_ABI_VERSION 3\n" in open(HEADER).read()
+    assert lib.lsd_abi_version() == 4 == binding.ABI_VERSION
+    assert "#define LSD_ABI_VERSION 4\n" in open(HEADER).read()
     for st in range(9):
         assert lib.lsd_status_str(st).decode()
     assert lib.lsd_status_str(99).decode() == "unknown status"
@@ -91,7 +91,7 @@ def test_prep_ex_argument_errors(lib):
     f = lib.qk_prep_fp4_ex
     ws = ctypes.c_void_p(0x200000)
     need = lib.qk_prep_fp4_workspace_bytes(2, 16, 128)
-    assert f(A, A, A, A, A, A, A, ws, need, 2, 16, 128, 4, N) == 8         # unknown flag bit
+    assert f(A, A, A, A, A, A, A, ws, need, 2, 16, 128, 8, N) == 8         # unknown flag bit
     assert f(A, A, A, A, A, A, A, ws, need, 2, 16, 128, -1, N) == 8
     assert f(A, A, A, A, A, A, A, ws, need, 2, 16, 64, 3, N) == 3
     assert f(A, A, A, A, A, A, N, ws, need, 2, 16, 128, 1, N) == 1         # smoothing needs k_mean
@@ -108,15 +108,43 @@ def test_fp4qk_argument_errors(lib):
     assert f(A, A, A, A, A, A, N, 2, 16, 256, 0.1, N) == 3
 
 
+def test_fused_q_argument_errors(lib):
+    f = lib.attn_fwd_fp4qk_fused_q
+    ok = [A] * 5
+    assert f(*ok, N, 2, 16, 256, 0.1, N) == 3                           # d
+    assert f(*ok, N, 2, 1 << 23, 128, 0.1, N) == 2                      # one head too long
+    for i in range(5):
+        args = list(ok)
+        args[i] = N
+        assert f(*args, N, 2, 16, 128, 0.1, N) == 1, i
+    args = list(ok)
+    args[0] = B
+    assert f(*args, N, 2, 16, 128, 0.1, N) == 4
+    assert f(*ok, ctypes.c_void_p(0x100002), 2, 16, 128, 0.1, N) == 4   # lse alignment
+    assert f(*ok, N, 2, 16, 128, float("inf"), N) == 7
+
+
+def test_k_only_prep_flag_errors(lib):
+    f = lib.qk_prep_fp4_ex
+    ws = ctypes.c_void_p(0x200000)
+    need = lib.qk_prep_fp4_workspace_bytes(2, 16, 128)
+    # K's pointers stay required; an unknown bit is still rejected
+    assert f(N, N, N, N, N, A, A, ws, need, 2, 16, 128, 7, N) == 1      # k NULL
+    assert f(N, A, N, N, A, N, A, ws, need, 2, 16, 128, 7, N) == 1      # k_scales NULL
+    assert f(N, A, N, N, A, A, N, ws, need, 2, 16, 128, 7, N) == 1      # k_mean NULL with smoothing
+    assert f(N, A, N, N, A, A, A, ws, need, 2, 16, 128, 15, N) == 8     # unknown bit 8
+    assert f(N, A, N, N, A, A, A, ws, need - 1, 2, 16, 128, 7, N) == 5  # workspace
+
+
 def test_missing_library_raises(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         binding.load_library(str(tmp_path / "nope.so"))
 
 
 def test_bwd_workspace_queries(lib):
-    assert lib.attn_bwd_bf16_workspace_bytes(40, 109000, 128) == 2 * 40 * 109000 * 4
+    assert lib.attn_bwd_bf16_workspace_bytes(40, 109000, 128) == 4 * 40 * 109000 * 4
     assert lib.attn_bwd_bf16_workspace_bytes(2, 16, 64) == 0
-    assert lib.attn_bwd_fp4qk_workspace_bytes(2, 16, 128) == 4 * 2 * 16 * 128 * 2 + 2 * 2 * 16 * 4
+    assert lib.attn_bwd_fp4qk_workspace_bytes(2, 16, 128) == 4 * 2 * 16 * 128 * 2 + 4 * 2 * 16 * 4
     assert lib.attn_bwd_fp4qk_workspace_bytes(0, 16, 128) == 0
 
 
@@ -124,18 +152,18 @@ def test_bwd_bf16_argument_errors(lib):
     f = lib.attn_bwd_bf16
     ws = ctypes.c_void_p(0x200000)
     need = lib.attn_bwd_bf16_workspace_bytes(2, 16, 128)
-    ok = [A] * 9
+    ok = [A] * 8
     assert f(*ok, ws, need, 2, 16, 64, 0.1, N) == 3                     # d
     assert f(*ok, ws, need, 2, 1 << 23, 128, 0.1, N) == 2               # one head too long
-    for i in range(9):                                                   # every pointer is required
+    for i in range(8):                                                   # every pointer is required
         args = list(ok)
         args[i] = N
         assert f(*args, ws, need, 2, 16, 128, 0.1, N) == 1, i
     args = list(ok)
-    args[4] = ctypes.c_void_p(0x100002)                                  # lse only needs 4-byte alignment
+    args[3] = ctypes.c_void_p(0x100002)                                  # lse only needs 4-byte alignment
     assert f(*args, ws, need, 2, 16, 128, 0.1, N) == 4
-    args[4] = ctypes.c_void_p(0x100004)
-    args[6] = B                                                          # dq misaligned
+    args[3] = ctypes.c_void_p(0x100004)
+    args[5] = B                                                          # dq misaligned
     assert f(*args, ws, need, 2, 16, 128, 0.1, N) == 4
     assert f(*ok, ws, need, 2, 16, 128, 0.0, N) == 7                    # scale
     assert f(*ok, N, need, 2, 16, 128, 0.1, N) == 5                     # workspace
@@ -146,10 +174,10 @@ def test_bwd_fp4qk_argument_errors(lib):
     f = lib.attn_bwd_fp4qk
     ws = ctypes.c_void_p(0x200000)
     need = lib.attn_bwd_fp4qk_workspace_bytes(2, 16, 128)
-    ok = [A] * 11
+    ok = [A] * 10
     assert f(*ok, ws, need, 2, 16, 128, 0.1, 4, N) == 8                 # unknown flag bit
     assert f(*ok, ws, need, 2, 16, 256, 0.1, 3, N) == 3
-    for i in range(11):
+    for i in range(10):
         args = list(ok)
         args[i] = N
         assert f(*args, ws, need, 2, 16, 128, 0.1, 3, N) == 1, i
@@ -185,7 +213,6 @@ def test_nvfp4_quantize_argument_errors(lib):
         assert f(A, A, A, 4, 32, 0.0, layout, N) == 7
         assert f(A, A, A, 4, 32, -2.0, layout, N) == 7
         assert f(A, A, A, 4, 32, float("inf"), layout, N) == 7
-        assert f(A, A, A, 4, 32, 1e-45, layout, N) == 7                 # 1/g overflows float32
     assert f(A, A, A, 4, 32, 1.0, 2, N) == 8                            # unknown layout
     assert f(A, A, A, 4, 32, 1.0, -1, N) == 8
 
@@ -195,6 +222,8 @@ def test_nvfp4_linear_argument_errors(lib):
     for layout in (0, 1):
         assert f(A, A, 1.0, A, A, 1.0, A, 0, 8, 64, layout, N) == 2     # M
         assert f(A, A, 1.0, A, A, 1.0, A, 8, 0, 64, layout, N) == 2     # N
+        assert f(A, A, 1.0, A, A, 1.0, A, 2 ** 31 - 255, 8, 64, layout, N) == 2    # M: tile count overflows
+        assert f(A, A, 1.0, A, A, 1.0, A, 8, 2 ** 31 - 1, 64, layout, N) == 2      # N: tile count overflows
         assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, 8, layout, N) == 2      # K < 16
         assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, 72, layout, N) == 2     # K not a multiple of 16
         assert f(A, A, 1.0, A, A, 1.0, A, 8, 8, (1 << 20) + 16, layout, N) == 2    # K too large

@@ -186,3 +186,35 @@ def test_fp4_ste_rotation_and_mean_terms():
         fd[idx] = (f(k0 + e) - f(k0 - e)) / 2e-3
         assert abs(fd[idx] - dk[0][idx]) <= 1e-9 * (1 + abs(dk[0][idx]))
     assert np.max(np.abs(dkh.sum(axis=1))) <= 1e-12 * np.abs(dkh).sum()
+
+
+def test_row_stats_and_key_subset_equal_the_full_gradient():
+    # the forms used for sampled checks at full size: per-query LSE and D over
+    # all keys, then dK, dV of a subset of keys from every query
+    from oracle.attention_bwd import attention_bwd_keys_fp64, attention_row_stats_fp64
+    rng = np.random.default_rng(40)
+    L, d = 300, 16
+    q, k, v, do = (rng.standard_normal((1, L, d)) * s for s in (2.0, 2.0, 1.0, 1.0))
+    scale = 0.7
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, scale)
+    lse, dsum = attention_row_stats_fp64(q[0], k[0], v[0], do[0], scale)
+    o, lse_ref = attention_fp64(q, k, v, scale)
+    assert np.allclose(lse, lse_ref[0], rtol=0, atol=1e-12)
+    assert np.allclose(dsum, (do[0] * o[0]).sum(axis=1), rtol=1e-12, atol=1e-12)
+    keys = np.array([0, 1, 77, 150, 299])
+    gk, gv = attention_bwd_keys_fp64(q[0], k[0], v[0], do[0], scale, keys, lse, dsum, block=64)
+    assert np.allclose(gk, dk[0, keys], rtol=1e-10, atol=1e-12)
+    assert np.allclose(gv, dv[0, keys], rtol=1e-10, atol=1e-12)
+    # a D taken from another row, or an LSE off by a constant, changes dK
+    bad_k, _ = attention_bwd_keys_fp64(q[0], k[0], v[0], do[0], scale, keys, lse, np.roll(dsum, 1))
+    assert not np.allclose(bad_k, dk[0, keys], rtol=1e-3, atol=1e-6)
+    _, bad_v = attention_bwd_keys_fp64(q[0], k[0], v[0], do[0], scale, keys, lse + 0.01, dsum)
+    assert not np.allclose(bad_v, dv[0, keys], rtol=1e-3, atol=1e-6)
+
+
+def test_hadamard_orthonormal():
+    from oracle.attention_bwd import hadamard_orthonormal
+    for d in (2, 16, 128):
+        r = hadamard_orthonormal(d)
+        assert np.allclose(r @ r, np.eye(d), atol=1e-14) and np.array_equal(r, r.T)
+        assert np.array_equal(np.rint(r * np.sqrt(d)).astype(np.int64), sylvester(d))
