@@ -155,6 +155,30 @@ int qk_prep_fp4_ex(const uint16_t* q, const uint16_t* k,
                    float* k_mean, void* workspace, size_t workspace_bytes,
                    int H, int L, int d, int flags, void* stream);
 
+/* Largest problem qk_prep_fp4_noalloc accepts: its static scratch holds the
+ * prep's exact partial column sums, 16384 bytes per (head, 4096-token chunk
+ * of L), i.e. H * ceil(L / 4096) <= 4096 (64 MiB per GPU). */
+#define LSD_PREP_NOALLOC_MAX_HEAD_CHUNKS 4096
+
+/*
+ * qk_prep_fp4_noalloc - qk_prep_fp4 without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, outputs,
+ * layouts, bit-exact results and errors as qk_prep_fp4, minus the workspace.
+ * Its scratch is a static 64 MiB device array inside the library (one per
+ * GPU, held until the process ends); the first call on a device looks up that
+ * device's copy (no allocation).  H * ceil(L / 4096) above
+ * LSD_PREP_NOALLOC_MAX_HEAD_CHUNKS -> LSD_ERR_WORKSPACE, before anything is
+ * enqueued.  Every call on one GPU uses the same scratch: calls that overlap
+ * in time on one GPU (different streams, different host threads) race and
+ * must be ordered by the caller.  Nothing in the scratch needs clearing
+ * between calls (each call writes every value it reads).
+ */
+int qk_prep_fp4_noalloc(const uint16_t* q, const uint16_t* k,
+                        uint8_t* q_codes, uint8_t* q_scales,
+                        uint8_t* k_codes, uint8_t* k_scales,
+                        float* k_mean, int H, int L, int d, void* stream);
+
 /*
  * attn_fwd_fp4qk - attention on quantized Q and K.
  *   q_codes, q_scales, k_codes, k_scales : as written by qk_prep_fp4 (or by

@@ -39,6 +39,7 @@ SIGNATURES = {
     "qk_prep_fp4_workspace_bytes": (_S, [_I, _I, _I]),
     "qk_prep_fp4": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _P]),
     "qk_prep_fp4_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _P]),
+    "qk_prep_fp4_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "attn_fwd_fp4qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
     "attn_fwd_fp4qk_fused_q": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
     "attn_bwd_bf16_workspace_bytes": (_S, [_I, _I, _I]),
@@ -199,6 +200,21 @@ def qk_prep_fp4_ex(q, k, flags, out=None, workspace=None, stream=None):
         _ptr(out["k_scales"]), _ptr(out["k_mean"]), _ptr(workspace), nbytes, H, L, d, int(flags),
         _stream(stream))
     _check("qk_prep_fp4_ex", st)
+    return out
+
+
+def qk_prep_fp4_noalloc(q, k, out, stream=None):
+    """qk_prep_fp4 with the library's static scratch instead of a workspace;
+    ``out`` (the dict of qk_prep_fp4's outputs) must be given: nothing is
+    allocated."""
+    H, L, d = q.shape
+    if out is None:
+        raise ValueError("qk_prep_fp4_noalloc allocates nothing: pass the output tensors")
+    out = _prep_outputs(q, k, out)
+    st = load_library().qk_prep_fp4_noalloc(
+        _ptr(q), _ptr(k), _ptr(out["q_codes"]), _ptr(out["q_scales"]), _ptr(out["k_codes"]),
+        _ptr(out["k_scales"]), _ptr(out["k_mean"]), H, L, d, _stream(stream))
+    _check("qk_prep_fp4_noalloc", st)
     return out
 
 

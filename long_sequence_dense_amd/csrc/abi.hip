@@ -100,6 +100,22 @@ int qk_prep_fp4(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8_t*
                         LSD_PREP_SMOOTH_K | LSD_PREP_ROTATE, stream);
 }
 
+int qk_prep_fp4_noalloc(const uint16_t* q, const uint16_t* k, uint8_t* q_codes, uint8_t* q_scales,
+                        uint8_t* k_codes, uint8_t* k_scales, float* k_mean, int H, int L, int d, void* stream) {
+  int st = check_shape(H, L, d);
+  if (st != LSD_OK) return st;
+  if (!q || !k || !q_codes || !q_scales || !k_codes || !k_scales || !k_mean) return LSD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_codes) || !aligned16(q_scales) ||
+      !aligned16(k_codes) || !aligned16(k_scales) || !aligned16(k_mean))
+    return LSD_ERR_ALIGN;
+  if (lsd::prep_workspace_bytes(H, L) > lsd::prep_scratch_bytes()) return LSD_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (lsd::prep_scratch(&scratch) != hipSuccess) return LSD_ERR_LAUNCH;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_qk_prep(q, k, q_codes, q_scales, k_codes, k_scales, k_mean, scratch, H, L,
+                                           true, true, true, (hipStream_t)stream));
+}
+
 int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
                    const uint8_t* k_scales, const uint16_t* v, uint16_t* o, float* lse, int H, int L,
                    int d, float softmax_scale, void* stream) {

@@ -34,6 +34,10 @@ hipError_t launch_attn_bwd_fp4qk(const uint8_t* qc, const uint8_t* qs, const uin
 
 // Q/K preparation (qk_prep.hip)
 size_t prep_workspace_bytes(int H, int L);
+// The prep's static scratch (no-allocation entry point): its capacity in bytes,
+// and this device's address of it (looked up once per device).
+size_t prep_scratch_bytes();
+hipError_t prep_scratch(void** ptr);
 hipError_t launch_qk_prep(const uint16_t* q, const uint16_t* k, uint8_t* qc, uint8_t* qs,
                           uint8_t* kc, uint8_t* ks, float* kmean, void* ws, int H, int L,
                           bool smooth, bool rotate, bool with_q, hipStream_t stream);

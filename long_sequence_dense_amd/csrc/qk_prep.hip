@@ -39,9 +39,12 @@
 // after the two transforms): without smoothing the mean kernels are skipped
 // and K is quantized as given; without the rotation the butterfly and the
 // 1/sqrt(128) factor are skipped and each block is 16 consecutive channels.
+#include <mutex>
+
 #include "lsd_internal.h"
 #include "device_common.h"
 #include "nvfp4_quant.h"
+#include "../../include/lsd_attn.h"
 
 namespace lsd {
 namespace {
@@ -547,6 +550,37 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, uint8_t* codes, uint8_t* sca
   hipLaunchKernelGGL(nvfp4_quant_rows_kernel, dim3((unsigned)grid), dim3(QUANT_THREADS), 0, stream, x, codes, scales,
                      nblocks, r);
   return hipGetLastError();
+}
+
+// Static scratch of the no-allocation prep: the exact partial column sums of K
+// for up to LSD_PREP_NOALLOC_MAX_HEAD_CHUNKS (head, 4096-token chunk) pairs.
+// In host code `scratch` names a host-side stand-in; the device address of
+// each GPU's copy comes from hipGetSymbolAddress on that device.
+constexpr size_t kScratchBytes = (size_t)LSD_PREP_NOALLOC_MAX_HEAD_CHUNKS * kHeadDim * MEAN_SLOTS * sizeof(double);
+static __device__ __align__(256) double scratch[kScratchBytes / sizeof(double)];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+size_t prep_scratch_bytes() { return kScratchBytes; }
+
+// This device's address of `scratch`, looked up on the first call with the
+// device current (the caller's current device), then kept.
+hipError_t prep_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 size_t prep_workspace_bytes(int H, int L) {

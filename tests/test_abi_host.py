@@ -100,6 +100,25 @@ def test_prep_ex_argument_errors(lib):
     assert f(A, A, N, A, A, A, N, N, 0, 2, 16, 128, 0, N) == 1             # null q_codes
 
 
+def test_noalloc_prep_argument_errors(lib):
+    # every rejection happens on the host, before the scratch is looked up
+    f = lib.qk_prep_fp4_noalloc
+    ok = [A] * 7
+    assert f(*ok, 2, 16, 64, N) == 3                                    # d
+    assert f(*ok, 0, 16, 128, N) == 2                                   # H
+    for i in range(7):                                                  # every pointer is required
+        args = list(ok)
+        args[i] = N
+        assert f(*args, 2, 16, 128, N) == 1, i
+    args = list(ok)
+    args[6] = B                                                         # k_mean misaligned
+    assert f(*args, 2, 16, 128, N) == 4
+    # beyond the static scratch: H * ceil(L / 4096) > 4096
+    assert f(*ok, 4097, 16, 128, N) == 5
+    assert f(*ok, 40, 4096 * 103, 128, N) == 5
+    assert lib.qk_prep_fp4_workspace_bytes(40, 4096 * 102, 128) == 4080 * 128 * 16 * 8 <= 64 << 20
+
+
 def test_fp4qk_argument_errors(lib):
     f = lib.attn_fwd_fp4qk
     assert f(A, A, A, A, A, A, N, 2, 16, 128, -1.0, N) == 7
