@@ -57,7 +57,7 @@ def gen_inputs(torch, name):
     return cfg, out
 
 
-KERNEL_SOURCES = ("attn_fwd.hip", "device_common.h", "lsd_internal.h")
+KERNEL_SOURCES = ("attn_fwd.hip", "device_common.h", "nvfp4_quant.h", "lsd_internal.h")
 
 
 def kernel_source_hash():
@@ -228,6 +228,28 @@ def config_path(torch, binding, stream, name, reps):
             "workload": cfg.desc, "in_value": False}
 
 
+def bw_ceiling(torch, H, L, d):
+    """Plain passes over a [H, L, d] BF16 tensor (one of the prep's inputs,
+    1.116 GB) with torch's own kernels: a read-only reduction (amax), a copy
+    (read + write) and a write-only fill of a code-sized buffer; 2 warm-ups, 5
+    timed calls each, HIP events on the current stream."""
+    stream = torch.cuda.current_stream()
+    x = torch.randn((H, L, d), device="cuda").to(torch.bfloat16)
+    y = torch.empty_like(x)
+    c = torch.empty((H, L, d // 2 + d // 16), dtype=torch.uint8, device="cuda")
+    nx, nc = x.numel() * 2, c.numel()
+    res = {}
+    for name, fn, nbytes in (("read_only_amax", lambda: x.amax(), nx),
+                             ("copy_read_write", lambda: y.copy_(x), 2 * nx),
+                             ("write_only_fill", lambda: c.fill_(7), nc)):
+        for _ in range(2):
+            fn()
+        t = time_calls(torch, stream, fn, n=5)
+        res[name] = {"ms": round(t, 4), "bytes": nbytes, "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    print(json.dumps({"bw_ceiling": res, "tensor": "[%d, %d, %d] bf16" % (H, L, d)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,6 +264,9 @@ def main():
                     help="skip the extra (not in value) timing of the NVFP4 linear layer")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the extra (not in value) BF16 timings of the 24 x 8192 and 40 x 36,480 workloads")
+    ap.add_argument("--bw-ceiling", action="store_true",
+                    help="time plain read-only, copy and write-only passes over tensors of the prep's sizes "
+                         "(the bandwidth ceiling its kernels are compared with); prints one JSON line")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for hardware-counter runs: one %d-byte torch copy (counter calibration), "
                          "then one launch of each kernel on the benchmark workload; no timing" % COPY_PROBE_BYTES)
@@ -257,6 +282,9 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     binding.load_library()
     H, L, d = 40, 109000, 128
+    if args.bw_ceiling:
+        bw_ceiling(torch, H, L, d)
+        return
 
     log("generating inputs (seeded, synthetic) ...")
     cfg4, x4 = gen_inputs(torch, "clip15s")
@@ -305,6 +333,12 @@ def main():
         b.copy_(a)                                   # the calibration copy
         torch.cuda.synchronize()
         step(False)
+        torch.cuda.synchronize()
+        kflags = binding.PREP_SMOOTH_K | binding.PREP_ROTATE | binding.PREP_K_ONLY
+        kprep = {key: prep[key] for key in ("k_codes", "k_scales", "k_mean")}
+        binding.qk_prep_fp4_ex(None, x5["k"], kflags, kprep, ws, stream)
+        binding.attn_fwd_fp4qk_fused_q(x5["q"], kprep["k_codes"], kprep["k_scales"], x5["v"], o5, None,
+                                       cfg5.scale, stream)
         torch.cuda.synchronize()
         x, w, gx, gw = linear_operands(torch, dev)
         T = binding.NVFP4_TILED
