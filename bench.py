@@ -411,8 +411,9 @@ def main():
         # Extra path, outside the step and its value: the backward of the BF16
         # path on the same inputs, dO ~ N(0, 1); 1 warm-up + 3 timed calls.
         log("timing attn_bwd_bf16 (3 calls) ...")
-        lse = torch.empty((H, L), dtype=torch.float32, device=dev)
-        binding.attn_fwd_bf16(x4["q"], x4["k"], x4["v"], o4, lse, cfg4.scale, stream)
+        o32 = torch.empty((H, L, d), dtype=torch.float32, device=dev)
+        ml = torch.empty((H, L, 2), dtype=torch.float32, device=dev)
+        binding.attn_fwd_bf16_train(x4["q"], x4["k"], x4["v"], o4, None, o32, ml, cfg4.scale, stream)
         gen = torch.Generator(device=dev)
         gen.manual_seed(5)
         dout = torch.randn((H, L, d), dtype=torch.float32, device=dev, generator=gen).to(torch.bfloat16)
@@ -423,7 +424,7 @@ def main():
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            binding.attn_bwd_bf16(x4["q"], x4["k"], x4["v"], lse, dout, *grads, softmax_scale=cfg4.scale,
+            binding.attn_bwd_bf16(x4["q"], x4["k"], x4["v"], o32, ml, dout, *grads, softmax_scale=cfg4.scale,
                                   workspace=bws, stream=stream)
             b.record(stream)
             b.synchronize()
@@ -434,17 +435,16 @@ def main():
         paths["attn_bwd_bf16"] = {"ms": round(t_bwd, 3), "TFLOP/s": round(bw, 1),
                                   "frac_of_peak": round(bw / PEAK_BF16_TFLOPS, 4),
                                   "flop_convention": "2.5 x forward (5 of the 2HL^2d products); the kernels "
-                                                     "compute 9 (S and dP in the row-statistics sweep, "
-                                                     "again for dK/dV and again for dQ)",
+                                                     "compute 7 (S and dP for dK/dV and again for dQ)",
                                   "in_value": False}
         # The training-time FP4 backward on the FP4 path's tensors (the codes
-        # of the step's prep, its forward's output and LSE): 1 warm-up + 2 calls.
+        # of the step's prep, its training forward's outputs): 1 warm-up + 2 calls.
         log("timing attn_bwd_fp4qk (2 calls) ...")
-        binding.attn_fwd_fp4qk(prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], x5["v"], o5,
-                               lse, cfg5.scale, stream)
+        binding.attn_fwd_fp4qk_train(prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], x5["v"],
+                                     o5, None, o32, ml, cfg5.scale, stream)
         fws = torch.empty(binding.attn_bwd_fp4qk_workspace_bytes(H, L, d), dtype=torch.uint8, device=dev)
         t_fb = time_calls(torch, stream, lambda: binding.attn_bwd_fp4qk(
-            prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], x5["v"], lse, dout, *grads,
+            prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], x5["v"], o32, ml, dout, *grads,
             softmax_scale=cfg5.scale, workspace=fws, stream=stream), n=2)
         fb = 2.5 * fl / (t_fb * 1e-3) / 1e12
         paths["attn_bwd_fp4qk"] = {"ms": round(t_fb, 3), "TFLOP/s": round(fb, 1),
@@ -452,7 +452,7 @@ def main():
                                    "flop_convention": "as attn_bwd_bf16; the time also covers the exact "
                                                       "dequantization of Q, K and the rotation of dQ, dK back",
                                    "in_value": False}
-        del grads, dout, bws, fws
+        del grads, dout, bws, fws, o32, ml
     if args.only != "bf16" and not args.no_linear:
         # Extra path, outside the step and its value: one NVFP4 W4A4 linear of
         # the same transformer at the 40 x 128 hidden size, over the clip's

@@ -11,6 +11,9 @@
  *   attn_fwd_fp4qk  attention whose scores come from the NVFP4 Q and K;
  *                   probabilities and V stay BF16 (attn_fwd_fp4qk_fused_q:
  *                   the same with Q quantized inside the attention kernel).
+ *   attn_fwd_bf16_train, attn_fwd_fp4qk_train  the two forwards with the
+ *                   extra outputs their backward reads (fp32 O, row max and
+ *                   row sum).
  *   attn_bwd_bf16   gradients of attn_fwd_bf16 with respect to Q, K and V.
  *   attn_bwd_fp4qk  training-time gradients of attn_fwd_fp4qk (straight-
  *                   through quantizer), with respect to the original Q, K, V.
@@ -68,7 +71,7 @@ enum lsd_status {
 };
 
 /* Version of this ABI (the value of LSD_ABI_VERSION the library was built with). */
-#define LSD_ABI_VERSION 4
+#define LSD_ABI_VERSION 5
 int lsd_abi_version(void);
 
 /* Static description of a status code ("ok", "null pointer", ...). */
@@ -89,6 +92,24 @@ const char* lsd_status_str(int status);
 int attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   uint16_t* o, float* lse, int H, int L, int d,
                   float softmax_scale, void* stream);
+
+/*
+ * attn_fwd_bf16_train - attn_fwd_bf16 (the same o and optional lse, bit for
+ * bit) that also writes what attn_bwd_bf16 reads:
+ *   o_f32  : [H, L, d] float32, written: the fp32 values that o rounds (o is
+ *            their round to nearest even), 16-byte aligned.
+ *   row_ml : [H, L, 2] float32, written: per query row the pair (m, l) with
+ *            the row's weights exp2(sigma log2(e) s_j - m) / l, m the
+ *            reference max in log2 units and l the sum of the BF16-rounded
+ *            weights that o is normalized by; 8-byte aligned.
+ * The pair replaces one fp32 log-sum-exp, whose rounding (the scores reach
+ * ~1e5 in log2 units on peaked workloads) would shift every recomputed
+ * weight of a row.  Errors as attn_fwd_bf16; o_f32 and row_ml are required.
+ * Source: "NVFP4 QAD" (training with the deployed attention in the loop).
+ */
+int attn_fwd_bf16_train(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        uint16_t* o, float* lse, float* o_f32, float* row_ml,
+                        int H, int L, int d, float softmax_scale, void* stream);
 
 /*
  * Bytes of device workspace qk_prep_fp4 needs for this shape (0 on a bad
@@ -199,6 +220,18 @@ int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales,
                    int H, int L, int d, float softmax_scale, void* stream);
 
 /*
+ * attn_fwd_fp4qk_train - attn_fwd_fp4qk (the same o and optional lse, bit for
+ * bit) that also writes o_f32 and row_ml exactly as attn_fwd_bf16_train does;
+ * attn_bwd_fp4qk reads them.
+ * Source: "NVFP4 QAD", "FP4 attention" (the training-time FP4 attention).
+ */
+int attn_fwd_fp4qk_train(const uint8_t* q_codes, const uint8_t* q_scales,
+                         const uint8_t* k_codes, const uint8_t* k_scales,
+                         const uint16_t* v, uint16_t* o, float* lse,
+                         float* o_f32, float* row_ml,
+                         int H, int L, int d, float softmax_scale, void* stream);
+
+/*
  * attn_fwd_fp4qk_fused_q - attn_fwd_fp4qk with Q's preparation done inside
  * the attention kernel: each workgroup rotates and quantizes its own query
  * rows (the arithmetic of qk_prep_fp4, so the same codes) and dequantizes them
@@ -219,17 +252,15 @@ int attn_fwd_fp4qk_fused_q(const uint16_t* q, const uint8_t* k_codes,
 
 /*
  * Bytes of device workspace attn_bwd_bf16 needs (0 on a bad shape):
- * 4 * H * L * 4 (four fp32 statistics per query row).
+ * 3 * H * L * 4 (three fp32 statistics per query row).
  */
 size_t attn_bwd_bf16_workspace_bytes(int H, int L, int d);
 
 /*
  * attn_bwd_bf16 - gradients of attn_fwd_bf16 with respect to Q, K and V.
  *   q, k, v : [H, L, d] BF16 bits, the forward's inputs.
- *   lse     : [H, L] float32, the forward's natural-log LSE (required): only
- *             the reference shift of the recomputed probabilities, which the
- *             backward normalizes itself (any value within a few units of
- *             the row's log-sum-exp gives the same gradients).
+ *   o_f32, row_ml : as written by attn_fwd_bf16_train on the same inputs and
+ *             softmax_scale (required).
  *   dout    : [H, L, d] BF16 bits, the gradient of the loss with respect to o.
  *   dq, dk, dv : [H, L, d] BF16 bits, written (round to nearest even of the
  *             fp32 results).  Must not alias any input.
@@ -238,26 +269,25 @@ size_t attn_bwd_bf16_workspace_bytes(int H, int L, int d);
  *   softmax_scale : the sigma of the forward.
  * With P = softmax(sigma Q K^T) row-wise: dV = P^T dO, dP = dO V^T,
  * D = rowsum(P * dP), dS = P * (dP - D), dQ = sigma dS K, dK = sigma dS^T Q.
- * A first sweep over the keys forms each row's normalization and D from the
- * same fp32 scores and dP that the gradient sweeps recompute, so D is a
- * normalized mean of the row's dP under the same weights (the forward's
- * output is not needed); D is kept relative to the dP of the row's dominant
- * key, so rows that put nearly all their weight on one key keep the relative
- * accuracy of their (nearly zero) dS.  P and dS are rounded to BF16 for the matrix-core
- * products; sums are fp32.  Nine of the 2 H L^2 d products per call.
- * Deterministic (no atomics).  Same shape limits as attn_fwd_bf16.
+ * P is recomputed as exp2(sigma log2(e) s - m) / l from row_ml, and
+ * D = rowsum(dO * O) from the fp32 O, which is the average of dP under the
+ * forward's own weights: on rows that put nearly all their weight on one key
+ * (dS nearly zero) dP - D then carries fp32 rounding only, where a BF16 O
+ * would leave an error of 2^-9 |dP|.  P and dS are rounded to BF16 for the
+ * matrix-core products; sums are fp32.  Seven of the 2 H L^2 d products per
+ * call.  Deterministic (no atomics).  Same shape limits as attn_fwd_bf16.
  * Source: "NVFP4 QAD" and "FP4 attention" (the model is trained with the
  * deployed attention in the loop); the gradients are those of the forward.
  */
 int attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                  const float* lse, const uint16_t* dout,
+                  const float* o_f32, const float* row_ml, const uint16_t* dout,
                   uint16_t* dq, uint16_t* dk, uint16_t* dv,
                   void* workspace, size_t workspace_bytes,
                   int H, int L, int d, float softmax_scale, void* stream);
 
 /*
  * Bytes of device workspace attn_bwd_fp4qk needs (0 on a bad shape):
- * 4 * H * L * d * 2 + 4 * H * L * 4 (dequantized Q, K and their gradients in
+ * 4 * H * L * d * 2 + 3 * H * L * 4 (dequantized Q, K and their gradients in
  * BF16, and the row statistics).
  */
 size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d);
@@ -266,9 +296,9 @@ size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d);
  * attn_bwd_fp4qk - training-time gradients of attn_fwd_fp4qk, with the NVFP4
  * quantizer passed straight through (its gradient taken as the identity).
  *   q_codes, q_scales, k_codes, k_scales : as written by qk_prep_fp4(_ex).
- *   v, lse  : the forward's V (BF16) and the natural-log LSE written by
- *             attn_fwd_fp4qk (required; the reference shift, as for
- *             attn_bwd_bf16).
+ *   v       : the forward's V (BF16).
+ *   o_f32, row_ml : as written by attn_fwd_fp4qk_train on the same codes
+ *             (required).
  *   dout      : [H, L, d] BF16, the gradient of the loss with respect to o.
  *   dq, dk    : [H, L, d] BF16, written: gradients with respect to the
  *             ORIGINAL Q and K (before smoothing and rotation).
@@ -288,7 +318,7 @@ size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d);
  */
 int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales,
                    const uint8_t* k_codes, const uint8_t* k_scales,
-                   const uint16_t* v, const float* lse,
+                   const uint16_t* v, const float* o_f32, const float* row_ml,
                    const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                    void* workspace, size_t workspace_bytes,
                    int H, int L, int d, float softmax_scale, int flags, void* stream);

@@ -14,7 +14,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblsd_attn.so")
 HEAD_DIM = 128
-ABI_VERSION = 4         # LSD_ABI_VERSION of include/lsd_attn.h, which SIGNATURES mirrors
+ABI_VERSION = 5         # LSD_ABI_VERSION of include/lsd_attn.h, which SIGNATURES mirrors
 
 STATUS = {
     0: "LSD_OK", 1: "LSD_ERR_NULL", 2: "LSD_ERR_SHAPE", 3: "LSD_ERR_UNSUPPORTED_D",
@@ -36,16 +36,18 @@ SIGNATURES = {
     "lsd_abi_version": (_I, []),
     "lsd_status_str": (ctypes.c_char_p, [_I]),
     "attn_fwd_bf16": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
+    "attn_fwd_bf16_train": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
     "qk_prep_fp4_workspace_bytes": (_S, [_I, _I, _I]),
     "qk_prep_fp4": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _P]),
     "qk_prep_fp4_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _P]),
     "qk_prep_fp4_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "attn_fwd_fp4qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
+    "attn_fwd_fp4qk_train": (_I, [_P] * 9 + [_I, _I, _I, _F, _P]),
     "attn_fwd_fp4qk_fused_q": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P]),
     "attn_bwd_bf16_workspace_bytes": (_S, [_I, _I, _I]),
-    "attn_bwd_bf16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _F, _P]),
+    "attn_bwd_bf16": (_I, [_P] * 10 + [_S, _I, _I, _I, _F, _P]),
     "attn_bwd_fp4qk_workspace_bytes": (_S, [_I, _I, _I]),
-    "attn_bwd_fp4qk": (_I, [_P] * 11 + [_S, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_fp4qk": (_I, [_P] * 12 + [_S, _I, _I, _I, _F, _I, _P]),
     "nvfp4_codes_bytes": (_S, [ctypes.c_longlong, _I, _I]),
     "nvfp4_scales_bytes": (_S, [ctypes.c_longlong, _I, _I]),
     "nvfp4_quantize": (_I, [_P, _P, _P, ctypes.c_longlong, _I, _F, _I, _P]),
@@ -138,6 +140,38 @@ def attn_fwd_bf16(q, k, v, o=None, lse=None, softmax_scale=None, stream=None):
                                       H, L, d, scale, _stream(stream))
     _check("attn_fwd_bf16", st)
     return o
+
+
+def _train_outputs(H, L, d, device, o32, ml):
+    import torch
+    if o32 is None:
+        o32 = torch.empty((H, L, d), dtype=torch.float32, device=device)
+    if ml is None:
+        ml = torch.empty((H, L, 2), dtype=torch.float32, device=device)
+    _need(o32, "o32", (torch.float32,), (H, L, d))
+    _need(ml, "ml", (torch.float32,), (H, L, 2))
+    return o32, ml
+
+
+def attn_fwd_bf16_train(q, k, v, o=None, lse=None, o32=None, ml=None, softmax_scale=None, stream=None):
+    """attn_fwd_bf16 that also returns the backward's inputs: (o, o32, ml)
+    with o32 [H, L, 128] float32 and ml [H, L, 2] float32 (row max m, row sum
+    l)."""
+    import torch
+    H, L, d = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, n, _bf16_types(), (H, L, d))
+    if o is None:
+        o = torch.empty((H, L, d), dtype=torch.bfloat16, device=q.device)
+    _need(o, "o", _bf16_types(), (H, L, d))
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), (H, L))
+    o32, ml = _train_outputs(H, L, d, q.device, o32, ml)
+    scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    st = load_library().attn_fwd_bf16_train(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o32), _ptr(ml),
+                                            H, L, d, scale, _stream(stream))
+    _check("attn_fwd_bf16_train", st)
+    return o, o32, ml
 
 
 def qk_prep_fp4_workspace_bytes(H, L, d=HEAD_DIM):
@@ -240,6 +274,30 @@ def attn_fwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o=None, lse=None,
     return o
 
 
+def attn_fwd_fp4qk_train(q_codes, q_scales, k_codes, k_scales, v, o=None, lse=None, o32=None, ml=None,
+                         softmax_scale=None, stream=None):
+    """attn_fwd_fp4qk that also returns the backward's inputs: (o, o32, ml)."""
+    import torch
+    H, L, d = v.shape
+    _need(v, "v", _bf16_types(), (H, L, d))
+    for n, t in (("q_codes", q_codes), ("k_codes", k_codes)):
+        _need(t, n, (torch.uint8,), (H, L, d // 2))
+    for n, t in (("q_scales", q_scales), ("k_scales", k_scales)):
+        _need(t, n, (torch.uint8,), (H, L, d // 16))
+    if o is None:
+        o = torch.empty((H, L, d), dtype=torch.bfloat16, device=v.device)
+    _need(o, "o", _bf16_types(), (H, L, d))
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), (H, L))
+    o32, ml = _train_outputs(H, L, d, v.device, o32, ml)
+    scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    st = load_library().attn_fwd_fp4qk_train(_ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales),
+                                             _ptr(v), _ptr(o), _ptr(lse), _ptr(o32), _ptr(ml), H, L, d, scale,
+                                             _stream(stream))
+    _check("attn_fwd_fp4qk_train", st)
+    return o, o32, ml
+
+
 def attn_fwd_fp4qk_fused_q(q, k_codes, k_scales, v, o=None, lse=None, softmax_scale=None, stream=None):
     """attn_fwd_fp4qk with Q ([H, L, 128] BF16) rotated and quantized inside
     the attention kernel; K as prepared by qk_prep_fp4_ex(..., PREP_K_ONLY |
@@ -266,14 +324,16 @@ def attn_bwd_bf16_workspace_bytes(H, L, d=HEAD_DIM):
     return int(load_library().attn_bwd_bf16_workspace_bytes(H, L, d))
 
 
-def attn_bwd_bf16(q, k, v, lse, dout, dq=None, dk=None, dv=None, softmax_scale=None,
+def attn_bwd_bf16(q, k, v, o32, ml, dout, dq=None, dk=None, dv=None, softmax_scale=None,
                   workspace=None, stream=None):
-    """Gradients (dq, dk, dv) of attn_fwd_bf16; lse is its LSE output."""
+    """Gradients (dq, dk, dv) of attn_fwd_bf16; o32 and ml as returned by
+    attn_fwd_bf16_train."""
     import torch
     H, L, d = q.shape
     for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need(t, n, _bf16_types(), (H, L, d))
-    _need(lse, "lse", (torch.float32,), (H, L))
+    _need(o32, "o32", (torch.float32,), (H, L, d))
+    _need(ml, "ml", (torch.float32,), (H, L, 2))
     outs = []
     for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is None:
@@ -284,7 +344,7 @@ def attn_bwd_bf16(q, k, v, lse, dout, dq=None, dk=None, dv=None, softmax_scale=N
         workspace = torch.empty(attn_bwd_bf16_workspace_bytes(H, L, d), dtype=torch.uint8, device=q.device)
     scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
     st = load_library().attn_bwd_bf16(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o32), _ptr(ml), _ptr(dout), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), H, L, d, scale, _stream(stream))
     _check("attn_bwd_bf16", st)
     return tuple(outs)
@@ -294,10 +354,11 @@ def attn_bwd_fp4qk_workspace_bytes(H, L, d=HEAD_DIM):
     return int(load_library().attn_bwd_fp4qk_workspace_bytes(H, L, d))
 
 
-def attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, lse, dout, dq=None, dk=None, dv=None,
+def attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o32, ml, dout, dq=None, dk=None, dv=None,
                    softmax_scale=None, flags=PREP_SMOOTH_K | PREP_ROTATE, workspace=None, stream=None):
     """Straight-through gradients (dq, dk, dv) of attn_fwd_fp4qk with respect
-    to the original Q, K and V; lse is the FP4-QK forward's LSE output."""
+    to the original Q, K and V; o32 and ml as returned by
+    attn_fwd_fp4qk_train."""
     import torch
     H, L, d = v.shape
     for n, t in (("v", v), ("dout", dout)):
@@ -306,7 +367,8 @@ def attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, lse, dout, dq=None, 
         _need(t, n, (torch.uint8,), (H, L, d // 2))
     for n, t in (("q_scales", q_scales), ("k_scales", k_scales)):
         _need(t, n, (torch.uint8,), (H, L, d // 16))
-    _need(lse, "lse", (torch.float32,), (H, L))
+    _need(o32, "o32", (torch.float32,), (H, L, d))
+    _need(ml, "ml", (torch.float32,), (H, L, 2))
     outs = []
     for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is None:
@@ -317,7 +379,7 @@ def attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, lse, dout, dq=None, 
         workspace = torch.empty(attn_bwd_fp4qk_workspace_bytes(H, L, d), dtype=torch.uint8, device=v.device)
     scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
     st = load_library().attn_bwd_fp4qk(
-        _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v), _ptr(lse), _ptr(dout),
+        _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v), _ptr(o32), _ptr(ml), _ptr(dout),
         _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(workspace), workspace.numel() * workspace.element_size(),
         H, L, d, scale, int(flags), _stream(stream))
     _check("attn_bwd_fp4qk", st)

@@ -62,7 +62,23 @@ int attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
   if (lse && ((uintptr_t)lse & 3u)) return LSD_ERR_ALIGN;
   if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
   (void)hipGetLastError();
-  return launch_status(lsd::launch_attn_bf16(q, k, v, o, lse, H, L, softmax_scale * kLog2e,
+  return launch_status(lsd::launch_attn_bf16(q, k, v, o, lse, nullptr, nullptr, H, L, softmax_scale * kLog2e,
+                                             (hipStream_t)stream));
+}
+
+int attn_fwd_bf16_train(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                        float* o_f32, float* row_ml, int H, int L, int d, float softmax_scale, void* stream) {
+  int st = check_shape(H, L, d);
+  if (st != LSD_OK) return st;
+  if ((st = check_attn_len(L)) != LSD_OK) return st;
+  if (!q || !k || !v || !o || !o_f32 || !row_ml) return LSD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(o_f32) ||
+      ((uintptr_t)row_ml & 7u))
+    return LSD_ERR_ALIGN;
+  if (lse && ((uintptr_t)lse & 3u)) return LSD_ERR_ALIGN;
+  if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_attn_bf16(q, k, v, o, lse, o_f32, row_ml, H, L, softmax_scale * kLog2e,
                                              (hipStream_t)stream));
 }
 
@@ -129,8 +145,25 @@ int attn_fwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_
   if (lse && ((uintptr_t)lse & 3u)) return LSD_ERR_ALIGN;
   if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
   (void)hipGetLastError();
-  return launch_status(lsd::launch_attn_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, H, L,
-                                              softmax_scale * kLog2e, (hipStream_t)stream));
+  return launch_status(lsd::launch_attn_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, nullptr, nullptr,
+                                              H, L, softmax_scale * kLog2e, (hipStream_t)stream));
+}
+
+int attn_fwd_fp4qk_train(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                         const uint8_t* k_scales, const uint16_t* v, uint16_t* o, float* lse, float* o_f32,
+                         float* row_ml, int H, int L, int d, float softmax_scale, void* stream) {
+  int st = check_shape(H, L, d);
+  if (st != LSD_OK) return st;
+  if ((st = check_attn_len(L)) != LSD_OK) return st;
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v || !o || !o_f32 || !row_ml) return LSD_ERR_NULL;
+  if (!aligned16(q_codes) || !aligned16(q_scales) || !aligned16(k_codes) || !aligned16(k_scales) ||
+      !aligned16(v) || !aligned16(o) || !aligned16(o_f32) || ((uintptr_t)row_ml & 7u))
+    return LSD_ERR_ALIGN;
+  if (lse && ((uintptr_t)lse & 3u)) return LSD_ERR_ALIGN;
+  if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
+  (void)hipGetLastError();
+  return launch_status(lsd::launch_attn_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o, lse, o_f32, row_ml,
+                                              H, L, softmax_scale * kLog2e, (hipStream_t)stream));
 }
 
 int attn_fwd_fp4qk_fused_q(const uint16_t* q, const uint8_t* k_codes, const uint8_t* k_scales, const uint16_t* v,
@@ -153,22 +186,22 @@ size_t attn_bwd_bf16_workspace_bytes(int H, int L, int d) {
   return lsd::attn_bwd_workspace_bytes(H, L);
 }
 
-int attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
-                  const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
-                  size_t workspace_bytes, int H, int L, int d, float softmax_scale, void* stream) {
+int attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* o_f32,
+                  const float* row_ml, const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                  void* workspace, size_t workspace_bytes, int H, int L, int d, float softmax_scale, void* stream) {
   int st = check_shape(H, L, d);
   if (st != LSD_OK) return st;
   if ((st = check_attn_len(L)) != LSD_OK) return st;
-  if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv) return LSD_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
+  if (!q || !k || !v || !o_f32 || !row_ml || !dout || !dq || !dk || !dv) return LSD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_f32) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)row_ml & 7u))
     return LSD_ERR_ALIGN;
   if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lsd::attn_bwd_workspace_bytes(H, L))
     return LSD_ERR_WORKSPACE;
   (void)hipGetLastError();
-  return launch_status(lsd::launch_attn_bwd(q, k, v, lse, dout, dq, dk, dv, workspace, H, L, softmax_scale,
-                                            (hipStream_t)stream));
+  return launch_status(lsd::launch_attn_bwd(q, k, v, o_f32, row_ml, dout, dq, dk, dv, workspace, H, L,
+                                            softmax_scale, (hipStream_t)stream));
 }
 
 size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d) {
@@ -177,26 +210,26 @@ size_t attn_bwd_fp4qk_workspace_bytes(int H, int L, int d) {
 }
 
 int attn_bwd_fp4qk(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
-                   const uint8_t* k_scales, const uint16_t* v, const float* lse,
+                   const uint8_t* k_scales, const uint16_t* v, const float* o_f32, const float* row_ml,
                    const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace,
                    size_t workspace_bytes, int H, int L, int d, float softmax_scale, int flags, void* stream) {
   int st = check_shape(H, L, d);
   if (st != LSD_OK) return st;
   if ((st = check_attn_len(L)) != LSD_OK) return st;
   if (flags & ~(LSD_PREP_SMOOTH_K | LSD_PREP_ROTATE)) return LSD_ERR_FLAGS;
-  if (!q_codes || !q_scales || !k_codes || !k_scales || !v || !lse || !dout || !dq || !dk || !dv)
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v || !o_f32 || !row_ml || !dout || !dq || !dk || !dv)
     return LSD_ERR_NULL;
   if (!aligned16(q_codes) || !aligned16(q_scales) || !aligned16(k_codes) || !aligned16(k_scales) ||
-      !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
-      ((uintptr_t)lse & 3u))
+      !aligned16(v) || !aligned16(o_f32) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || ((uintptr_t)row_ml & 7u))
     return LSD_ERR_ALIGN;
   if ((st = check_scale(softmax_scale)) != LSD_OK) return st;
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lsd::attn_bwd_fp4qk_workspace_bytes(H, L))
     return LSD_ERR_WORKSPACE;
   (void)hipGetLastError();
-  return launch_status(lsd::launch_attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, lse, dout, dq, dk, dv,
-                                                  workspace, H, L, softmax_scale, (flags & LSD_PREP_ROTATE) != 0,
-                                                  (hipStream_t)stream));
+  return launch_status(lsd::launch_attn_bwd_fp4qk(q_codes, q_scales, k_codes, k_scales, v, o_f32, row_ml, dout,
+                                                  dq, dk, dv, workspace, H, L, softmax_scale,
+                                                  (flags & LSD_PREP_ROTATE) != 0, (hipStream_t)stream));
 }
 
 size_t nvfp4_codes_bytes(long long rows, int cols, int layout) {

@@ -8,26 +8,22 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
 //   dQ = sigma dS K,  dK = sigma dS^T Q.
 //
-// The backward recomputes the probabilities and normalizes them itself: the
-// forward's LSE serves only as a reference shift m_i (any value near the row's
-// log-sum-exp keeps exp2 in range), and a first sweep over the keys forms
-// l_i = sum_j exp2(s_ij c - m_i) and D_i = sum_j p_ij dP_ij / l_i from the
-// same fp32 scores and dP the gradient sweeps use.  D is then a normalized
-// weighted mean of the row's dP values under the backward's own weights, so
-// dP_ij - D_i is formed without cancellation against an independently rounded
-// output.  D is also kept relative to the dP of the row's dominant key (the
-// one key with a probability above 1/2, if there is one): the sweeps form
-// (dP_ij - dP_ref) - (D_i - dP_ref), which is exactly -(D_i - dP_ref) at that
-// key, so on rows where one key holds nearly all the weight (dS almost zero)
-// the gradient keeps its relative accuracy instead of an fp32 rounding of
-// dP_ij - D_i.
+// The probabilities are recomputed from the training forward's row
+// statistics: its reference max m_i and row sum l_i (kept apart rather than as
+// one fp32 log-sum-exp, whose rounding near m ~ 1e5 in log2 units would shift
+// every P of the row), as P_ij = exp2(s_ij c - m_i) / l_i.  D_i is formed from
+// the forward's fp32 output, D_i = sum_c dO_ic O_ic = sum_j w_ij dP_ij with the
+// forward's own weights w (the BF16-rounded exponentials over their sum, the
+// weights O was averaged with).  On a row that puts nearly all its weight on
+// one key, dP_ij - D_i at that key is then the small difference of two fp32
+// values that carry only fp32 rounding (no BF16 rounding of O enters), and the
+// remaining mismatch between P and w is the BF16 rounding of each weight,
+// which only rescales that key's already small dS.  (A BF16 O gives D an
+// error of 2^-9 |dP|, larger than dS itself on such rows.)
 //
 // Three launches, deterministic (no atomics):
-//   bwd_dq<stats>  the forward's layout: one wave per 32 queries, eight waves
-//               per workgroup; Q and dO of its rows in registers, 32-key tiles
-//               of K and V through LDS; S^T = K Q^T, dP^T = V dO^T on the
-//               32x32x16 BF16 MFMA; per row m = LSE log2(e), 1 / l, dP_ref
-//               and D - dP_ref into the workspace.
+//   bwd_rowstats  per query row: m, 1 / l and D from the forward's (m, l), its
+//               fp32 O and dO (16 lanes per row, a fixed reduction order).
 //   bwd_dkdv    one wave per 32 keys (eight waves, two per SIMD, per
 //               workgroup of 256 keys): K of its keys stays in registers and
 //               the workgroup's V rows in LDS, both read as MFMA B operands;
@@ -42,12 +38,14 @@
 //               (the accumulator layout is the operand layout up to a fixed
 //               permutation of the query index, which the transpose reads
 //               reproduce).
-//   bwd_dq<grad> the stats sweep's layout again: dS^T on the VALU,
-//               dQ^T += K^T dS^T.
+//   bwd_dq      the forward's layout: one wave per 32 queries, eight waves
+//               per workgroup; Q and dO of its rows in registers, 32-key tiles
+//               of K and V through LDS; S^T = K Q^T, dP^T = V dO^T, dS^T on
+//               the VALU, dQ^T += K^T dS^T.
+// Seven of the 2 H L^2 d products per call (S and dP twice, dV, dK, dQ).
 // P and dS are rounded to BF16 for their MFMAs; all sums are fp32.  Rows past
-// L are zero-filled by the buffer loads: their keys are masked out of the
-// row sums and add nothing to dQ (zero K rows), and their queries meet only
-// zero operands (the dQ sweeps give them weight zero).
+// L are zero-filled by the buffer loads: their keys add nothing to dQ (zero K
+// rows), and their queries have 1 / l = 0 (zero weights).
 #include "lsd_internal.h"
 #include "device_common.h"
 
@@ -183,7 +181,6 @@ struct DkdvParams {
   const float* dsum;
   const float* m2;
   const float* invl;
-  const float* dref;
   uint16_t* dk;
   uint16_t* dv;
   int L;
@@ -199,7 +196,6 @@ struct DkdvSmem {
   float m2[2][TR];
   float invl[2][TR];
   float dsum[2][TR];
-  float dref[2][TR];
   uint16_t v[DKDV_KEYS * VKS];          // the workgroup's V rows, read as B operands
 };
 
@@ -220,7 +216,6 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
   const Rsrc rm = make_rsrc(p.m2 + head_row0, (uint32_t)L * 4);
   const Rsrc ri = make_rsrc(p.invl + head_row0, (uint32_t)L * 4);
   const Rsrc rd = make_rsrc(p.dsum + head_row0, (uint32_t)L * 4);
-  const Rsrc rr = make_rsrc(p.dref + head_row0, (uint32_t)L * 4);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // This wave's 32 keys: K and V rows as B operands (8 chunks of 16 channels).
@@ -252,8 +247,8 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
   }
 
   // Query tile q0 into LDS buffer buf: each wave copies 4 rows of Q and of
-  // dO (one row per instruction), waves 0 to 3 the 32 values of m, D - dP_ref,
-  // 1 / l and dP_ref.  Rows past L arrive as zeros: their Q and dO rows are zero and
+  // dO (one row per instruction), waves 0 to 2 the 32 values of m, D and
+  // 1 / l.  Rows past L arrive as zeros: their Q and dO rows are zero and
   // their 1 / l is zero, so their probabilities and dS are zero.
   auto stage = [&](int q0, int buf) {
 #pragma unroll
@@ -266,7 +261,6 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
     if (wave_u == 0 && ln.lane < TR) dma_dword(rm, sm.m2[buf], 4 * (q0 + ln.lane));
     if (wave_u == 1 && ln.lane < TR) dma_dword(rd, sm.dsum[buf], 4 * (q0 + ln.lane));
     if (wave_u == 2 && ln.lane < TR) dma_dword(ri, sm.invl[buf], 4 * (q0 + ln.lane));
-    if (wave_u == 3 && ln.lane < TR) dma_dword(rr, sm.dref[buf], 4 * (q0 + ln.lane));
   };
 
   const int ntiles = (L + TR - 1) / TR;
@@ -296,13 +290,12 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
       const f32x4 m4 = *(const f32x4*)(&sm.m2[buf][8 * g + 4 * ln.hf]);
       const f32x4 i4 = *(const f32x4*)(&sm.invl[buf][8 * g + 4 * ln.hf]);
       const f32x4 d4 = *(const f32x4*)(&sm.dsum[buf][8 * g + 4 * ln.hf]);
-      const f32x4 r4 = *(const f32x4*)(&sm.dref[buf][8 * g + 4 * ln.hf]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * g + j;
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m4[j])) * i4[j];
         pf[i >> 3][i & 7] = pv;
-        df[i >> 3][i & 7] = pv * ((dp[i] - r4[j]) - d4[j]);
+        df[i >> 3][i & 7] = pv * (dp[i] - d4[j]);
       }
     }
     bf16x8 pb[2], dsb[2];
@@ -358,11 +351,9 @@ struct DqParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* lse;                             // the forward's LSE (natural log): the reference shift
-  float* dsum;                                  // per row: D - dP_ref, m = LSE log2(e), 1 / l, dP_ref
-  float* m2;                                    // (written by STATS)
-  float* invl;
-  float* dref;
+  const float* dsum;                            // per row: D, m, 1 / l (from bwd_rowstats)
+  const float* m2;
+  const float* invl;
   uint16_t* dq;
   int L;
   int n_qtiles;
@@ -375,17 +366,7 @@ struct DqSmem {
   uint16_t v[2][TILE];
 };
 
-// STATS: the first sweep, per row l = sum_j p_j with p_j = exp2(s_j c - m)
-// and n = sum_j p_j (dP_j - dP_ref) over the keys j < L, stored as m, 1 / l,
-// dP_ref and n / l = D - dP_ref.  dP_ref is the dP of the key whose p exceeds
-// 1/2 (m is the row's log-sum-exp, so p is its probability up to the LSE's
-// rounding; a later such key replaces an earlier one), 0 if there is none;
-// when it changes, n is moved to the new reference exactly as
-// n += l (dP_old - dP_new).  Otherwise the gradient sweep: P = p / l,
-// dS = P ((dP - dP_ref) - (D - dP_ref)), dQ^T += K^T dS^T.  Both sweeps compute
-// S^T and dP^T with the same instructions in the same order, so their fp32
-// values are the same.
-template <bool STATS>
+// P = exp2(s c - m) / l, dS = P (dP - D), dQ^T += K^T dS^T over the keys.
 __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
   __shared__ __attribute__((aligned(16))) DqSmem sm;
   const int tid = threadIdx.x;
@@ -417,16 +398,9 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
     }
   }
   // Rows past L: m = +inf, 1 / l = 0, so every weight is zero.
-  float m, invl = 0.0f, dsum = 0.0f, dref = 0.0f;
-  if constexpr (STATS) {
-    m = qvalid ? p.lse[head_row0 + qrow] * kLog2eF : __builtin_inff();
-  } else {
-    m = qvalid ? p.m2[head_row0 + qrow] : __builtin_inff();
-    invl = qvalid ? p.invl[head_row0 + qrow] : 0.0f;
-    dsum = qvalid ? p.dsum[head_row0 + qrow] : 0.0f;
-    dref = qvalid ? p.dref[head_row0 + qrow] : 0.0f;
-  }
-  float lsum = 0.0f, nsum = 0.0f, pref = 0.0f;
+  const float m = qvalid ? p.m2[head_row0 + qrow] : __builtin_inff();
+  const float invl = qvalid ? p.invl[head_row0 + qrow] : 0.0f;
+  const float dsum = qvalid ? p.dsum[head_row0 + qrow] : 0.0f;
   f32x16 dqacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) dqacc[db] = (f32x16)0.0f;
@@ -459,51 +433,20 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
     for (int kk = 0; kk < 8; ++kk) s = mfma(row_operand(kt, ln.lane_row, kk), qreg[kk], s);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) dp = mfma(row_operand(vt, ln.lane_row, kk), doreg[kk], dp);
-    if constexpr (STATS) {
-      const int kv0 = t * TR;
-      const bool ragged = kv0 + TR > L;
-      float pv[16], pmax = 0.0f;
+    f32x8 df[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m));
-        if (ragged && kv0 + 8 * (i >> 2) + 4 * ln.hf + (i & 3) >= L) pv[i] = 0.0f;
-        pmax = __builtin_fmaxf(pmax, pv[i]);
-      }
-      if (__builtin_expect(pmax > 0.5f, 0)) {     // a dominant key in this lane's part of the tile
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (pv[i] > 0.5f) {
-            nsum = __builtin_fmaf(lsum, dref - dp[i], nsum);
-            dref = dp[i];
-            pref = pv[i];
-          } else {
-            nsum = __builtin_fmaf(pv[i], dp[i] - dref, nsum);
-          }
-          lsum += pv[i];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          nsum = __builtin_fmaf(pv[i], dp[i] - dref, nsum);
-          lsum += pv[i];
-        }
-      }
-    } else {
-      f32x8 df[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m)) * invl;
-        df[i >> 3][i & 7] = pv * ((dp[i] - dref) - dsum);
-      }
-      bf16x8 dsb[2];
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) dsb[cc] = __builtin_convertvector(df[cc], bf16x8);
-      // dQ^T += K^T dS^T (keys past L: zero K rows add nothing)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dqacc[db] = mfma(tr_operand(kt, ln.lane_tr, cc, db), dsb[cc], dqacc[db]);
+    for (int i = 0; i < 16; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m)) * invl;
+      df[i >> 3][i & 7] = pv * (dp[i] - dsum);
     }
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) dsb[cc] = __builtin_convertvector(df[cc], bf16x8);
+    // dQ^T += K^T dS^T (keys past L: zero K rows add nothing)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) dqacc[db] = mfma(tr_operand(kt, ln.lane_tr, cc, db), dsb[cc], dqacc[db]);
 
     if (more) {
       store_rows(sm.k[buf ^ 1], tid, sk);
@@ -512,24 +455,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
     __syncthreads();
   }
 
-  if constexpr (STATS) {
-    // The two lane halves hold the same query's two key halves.  The half
-    // whose reference key has the larger p keeps its reference; the other
-    // half's n is moved onto it.
-    const float l2 = __shfl_xor(lsum, 32), n2 = __shfl_xor(nsum, 32);
-    const float r2 = __shfl_xor(dref, 32), p2 = __shfl_xor(pref, 32);
-    const bool mine = pref > p2 || (pref == p2 && ln.hf == 0);     // the same choice in both halves
-    const float rc = mine ? dref : r2;
-    const float nc = mine ? __builtin_fmaf(l2, r2 - rc, n2) + nsum : __builtin_fmaf(lsum, dref - rc, nsum) + n2;
-    const float lt = lsum + l2;
-    if (qvalid && ln.hf == 0) {
-      const float il = 1.0f / lt;
-      p.m2[head_row0 + qrow] = m;
-      p.invl[head_row0 + qrow] = il;
-      p.dsum[head_row0 + qrow] = nc * il;
-      p.dref[head_row0 + qrow] = rc;
-    }
-  } else if (qvalid) {
+  if (qvalid) {
     uint16_t* row = p.dq + (head_row0 + qrow) * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -541,6 +467,41 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
         *(u16x4*)(row + 32 * db + 8 * g + 4 * ln.hf) = w;
       }
     }
+  }
+}
+
+// ------------------------------------------------------------ row stats --
+
+constexpr int RS_THREADS = 256;                 // 16 lanes per row, 16 rows per workgroup
+
+// Per query row r: D = sum_c dO_rc O_rc (dO BF16, O the forward's fp32
+// output), m and 1 / l from the forward's (m, l).  Lane i of a row's 16 holds
+// channels 8 i .. 8 i + 7; the partial sums combine over xor distances 8, 4,
+// 2, 1 (a fixed order).  Rows past nrows return as whole groups of 16.
+__global__ __launch_bounds__(RS_THREADS) void bwd_rowstats_kernel(const float* __restrict__ o32,
+                                                                 const float* __restrict__ ml,
+                                                                 const uint16_t* __restrict__ dout,
+                                                                 float* __restrict__ dsum, float* __restrict__ m2,
+                                                                 float* __restrict__ invl, long long nrows) {
+  const int tid = threadIdx.x;
+  const int part = tid & 15;
+  const long long row = (long long)blockIdx.x * (RS_THREADS / 16) + (tid >> 4);
+  if (row >= nrows) return;
+  const u16x8 g = *(const u16x8*)(dout + row * kHeadDim + 8 * part);
+  const f32x4 a = *(const f32x4*)(o32 + row * kHeadDim + 8 * part);
+  const f32x4 b = *(const f32x4*)(o32 + row * kHeadDim + 8 * part + 4);
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(bf16_bits_to_f32(g[j]), a[j], acc);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(bf16_bits_to_f32(g[4 + j]), b[j], acc);
+#pragma unroll
+  for (int x = 8; x >= 1; x >>= 1) acc += __shfl_xor(acc, x);
+  if (part == 0) {
+    const float2 s = *(const float2*)(ml + 2 * row);
+    dsum[row] = acc;
+    m2[row] = s.x;
+    invl[row] = 1.0f / s.y;
   }
 }
 
@@ -628,41 +589,39 @@ __global__ __launch_bounds__(ROT_THREADS) void rotate_rows_kernel(const uint16_t
 
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(int H, int L) { return (size_t)4 * H * (size_t)L * sizeof(float); }
+size_t attn_bwd_workspace_bytes(int H, int L) { return (size_t)3 * H * (size_t)L * sizeof(float); }
 
 size_t attn_bwd_fp4qk_workspace_bytes(int H, int L) {
   return (size_t)4 * H * (size_t)L * kHeadDim * 2 + attn_bwd_workspace_bytes(H, L);
 }
 
-hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
-                           const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, int H, int L,
-                           float scale, hipStream_t stream) {
+hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* o32,
+                           const float* ml, const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws,
+                           int H, int L, float scale, hipStream_t stream) {
   const long long nrows = (long long)H * L;
   float* dsum = (float*)ws;
   float* m2 = dsum + nrows;
   float* invl = m2 + nrows;
-  float* dref = invl + nrows;
 
   DqParams b = {};
-  b.q = q; b.k = k; b.v = v; b.dout = dout; b.lse = lse; b.dsum = dsum; b.m2 = m2; b.invl = invl; b.dref = dref; b.dq = dq;
+  b.q = q; b.k = k; b.v = v; b.dout = dout; b.dsum = dsum; b.m2 = m2; b.invl = invl; b.dq = dq;
   b.L = L; b.n_qtiles = (L + DQ_ROWS - 1) / DQ_ROWS; b.c = scale * kLog2eF; b.scale = scale;
   const long long nq = (long long)b.n_qtiles * H;
-  if (nq > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)nq), dim3(DQ_THREADS), 0, stream, b);
-
   DkdvParams a = {};
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.dsum = dsum; a.m2 = m2; a.invl = invl; a.dref = dref; a.dk = dk; a.dv = dv;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.dsum = dsum; a.m2 = m2; a.invl = invl; a.dk = dk; a.dv = dv;
   a.L = L; a.n_ktiles = (L + DKDV_KEYS - 1) / DKDV_KEYS; a.c = scale * kLog2eF; a.scale = scale;
   const long long nk = (long long)a.n_ktiles * H;
-  if (nk > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)nk), dim3(DKDV_THREADS), 0, stream, a);
+  if (nq > 0x7FFFFFFFLL || nk > 0x7FFFFFFFLL) return hipErrorInvalidValue;
 
-  hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)nq), dim3(DQ_THREADS), 0, stream, b);
+  const unsigned rb = (unsigned)((nrows + (RS_THREADS / 16) - 1) / (RS_THREADS / 16));
+  hipLaunchKernelGGL(bwd_rowstats_kernel, dim3(rb), dim3(RS_THREADS), 0, stream, o32, ml, dout, dsum, m2, invl, nrows);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)nk), dim3(DKDV_THREADS), 0, stream, a);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)nq), dim3(DQ_THREADS), 0, stream, b);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                                 const uint16_t* v, const float* lse, const uint16_t* dout,
+                                 const uint16_t* v, const float* o32, const float* ml, const uint16_t* dout,
                                  uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, int H, int L, float scale,
                                  bool rotate, hipStream_t stream) {
   const long long nrows = (long long)H * L;
@@ -676,7 +635,7 @@ hipError_t launch_attn_bwd_fp4qk(const uint8_t* qc, const uint8_t* qs, const uin
   const unsigned db = (unsigned)((nblocks + DEQ_THREADS - 1) / DEQ_THREADS);
   hipLaunchKernelGGL(fp4_dequant_kernel, dim3(db), dim3(DEQ_THREADS), 0, stream, qc, qs, qh, nblocks);
   hipLaunchKernelGGL(fp4_dequant_kernel, dim3(db), dim3(DEQ_THREADS), 0, stream, kc, ks, kh, nblocks);
-  hipError_t e = launch_attn_bwd(qh, kh, v, lse, dout, rotate ? dqh : dq, rotate ? dkh : dk, dv, stats, H, L,
+  hipError_t e = launch_attn_bwd(qh, kh, v, o32, ml, dout, rotate ? dqh : dq, rotate ? dkh : dk, dv, stats, H, L,
                                  scale, stream);
   if (e != hipSuccess) return e;
   if (rotate) {

@@ -82,6 +82,8 @@ struct AttnParams {
   const uint8_t* ks;
   uint16_t* o;
   float* lse;
+  float* o32;                           // training outputs (both or neither): O in fp32,
+  float* ml;                            // and per row the reference max m and the sum l
   int L;
   int n_qtiles;
   float scale_log2;                     // softmax scale * log2(e)
@@ -545,6 +547,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
     }
     if (p.lse != nullptr && hf == 0)
       p.lse[head_row0 + qrow] = (st.m_used + __log2f(l_tot)) * 0.69314718055994530942f;
+    if (p.o32 != nullptr) {
+      // The fp32 quotients that were rounded to O above, and the row's
+      // (m, l): P_ij = exp2(s_ij c - m) / l reproduces the weights without an
+      // fp32 log-sum-exp (whose rounding near m ~ 1e5 would shift every P).
+      float* orow32 = p.o32 + (head_row0 + qrow) * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[j] = st.oacc[db][4 * g + j] * inv;
+          *(f32x4*)(orow32 + 32 * db + 8 * g + 4 * hf) = w;
+        }
+      if (hf == 0) *(float2*)(p.ml + 2 * (head_row0 + qrow)) = make_float2(st.m_used, l_tot);
+    }
   }
 }
 
@@ -563,18 +581,18 @@ hipError_t launch(const AttnParams& prm, bool fp4, bool quant_q, int H, hipStrea
 }  // namespace
 
 hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                            float* lse, int H, int L, float scale_log2, hipStream_t stream) {
+                            float* lse, float* o32, float* ml, int H, int L, float scale_log2, hipStream_t stream) {
   AttnParams prm = {};
-  prm.q = q; prm.k = k; prm.v = v; prm.o = o; prm.lse = lse;
+  prm.q = q; prm.k = k; prm.v = v; prm.o = o; prm.lse = lse; prm.o32 = o32; prm.ml = ml;
   prm.L = L; prm.n_qtiles = (L + BR - 1) / BR; prm.scale_log2 = scale_log2;
   return launch(prm, false, false, H, stream);
 }
 
 hipError_t launch_attn_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                             const uint16_t* v, uint16_t* o, float* lse, int H, int L, float scale_log2,
-                             hipStream_t stream) {
+                             const uint16_t* v, uint16_t* o, float* lse, float* o32, float* ml, int H, int L,
+                             float scale_log2, hipStream_t stream) {
   AttnParams prm = {};
-  prm.qc = qc; prm.qs = qs; prm.kc = kc; prm.ks = ks; prm.v = v; prm.o = o; prm.lse = lse;
+  prm.qc = qc; prm.qs = qs; prm.kc = kc; prm.ks = ks; prm.v = v; prm.o = o; prm.lse = lse; prm.o32 = o32; prm.ml = ml;
   prm.L = L; prm.n_qtiles = (L + BR - 1) / BR; prm.scale_log2 = scale_log2;
   return launch(prm, true, false, H, stream);
 }

@@ -9,26 +9,27 @@ namespace lsd {
 constexpr int kHeadDim = 128;
 constexpr int kBlock = 16;          // channels per NVFP4 scale
 
-// attention (attn_fwd.hip)
+// attention (attn_fwd.hip); o32 and ml (the training outputs) are both null
+// or both set
 hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                            uint16_t* o, float* lse, int H, int L, float scale_log2,
-                            hipStream_t stream);
+                            uint16_t* o, float* lse, float* o32, float* ml, int H, int L,
+                            float scale_log2, hipStream_t stream);
 hipError_t launch_attn_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
                              const uint8_t* ks, const uint16_t* v, uint16_t* o, float* lse,
-                             int H, int L, float scale_log2, hipStream_t stream);
+                             float* o32, float* ml, int H, int L, float scale_log2, hipStream_t stream);
 
 hipError_t launch_attn_fp4qk_fused_q(const uint16_t* q, const uint8_t* kc, const uint8_t* ks, const uint16_t* v,
                                      uint16_t* o, float* lse, int H, int L, float scale_log2, hipStream_t stream);
 
 // attention backward (attn_bwd.hip)
 size_t attn_bwd_workspace_bytes(int H, int L);
-hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
-                           const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, int H, int L,
-                           float scale, hipStream_t stream);
+hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* o32,
+                           const float* ml, const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws,
+                           int H, int L, float scale, hipStream_t stream);
 
 size_t attn_bwd_fp4qk_workspace_bytes(int H, int L);
 hipError_t launch_attn_bwd_fp4qk(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                                 const uint16_t* v, const float* lse, const uint16_t* dout,
+                                 const uint16_t* v, const float* o32, const float* ml, const uint16_t* dout,
                                  uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, int H, int L, float scale,
                                  bool rotate, hipStream_t stream);
 

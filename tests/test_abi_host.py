@@ -38,8 +38,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.lsd_abi_version() == 4 == binding.ABI_VERSION
-    assert "#define LSD_ABI_VERSION 4\n" in open(HEADER).read()
+    assert lib.lsd_abi_version() == 5 == binding.ABI_VERSION
+    assert "#define LSD_ABI_VERSION 5\n" in open(HEADER).read()
     for st in range(9):
         assert lib.lsd_status_str(st).decode()
     assert lib.lsd_status_str(99).decode() == "unknown status"
@@ -161,28 +161,50 @@ def test_missing_library_raises(tmp_path):
 
 
 def test_bwd_workspace_queries(lib):
-    assert lib.attn_bwd_bf16_workspace_bytes(40, 109000, 128) == 4 * 40 * 109000 * 4
+    assert lib.attn_bwd_bf16_workspace_bytes(40, 109000, 128) == 3 * 40 * 109000 * 4
     assert lib.attn_bwd_bf16_workspace_bytes(2, 16, 64) == 0
-    assert lib.attn_bwd_fp4qk_workspace_bytes(2, 16, 128) == 4 * 2 * 16 * 128 * 2 + 4 * 2 * 16 * 4
+    assert lib.attn_bwd_fp4qk_workspace_bytes(2, 16, 128) == 4 * 2 * 16 * 128 * 2 + 3 * 2 * 16 * 4
     assert lib.attn_bwd_fp4qk_workspace_bytes(0, 16, 128) == 0
+
+
+def test_train_forward_argument_errors(lib):
+    C = ctypes.c_void_p(0x100004)       # 4-byte aligned only
+    for f, nin in ((lib.attn_fwd_bf16_train, 3), (lib.attn_fwd_fp4qk_train, 5)):
+        ins = [A] * nin
+        # after the inputs: o, lse (optional), o_f32, row_ml; no call here passes every check
+        assert f(*ins, A, N, A, A, 2, 16, 256, 0.1, N) == 3             # d
+        assert f(*ins, A, N, A, A, 2, 1 << 23, 128, 0.1, N) == 2        # one head too long
+        assert f(*ins, A, N, N, A, 2, 16, 128, 0.1, N) == 1             # o_f32 required
+        assert f(*ins, A, N, A, N, 2, 16, 128, 0.1, N) == 1             # row_ml required
+        assert f(*ins, N, N, A, A, 2, 16, 128, 0.1, N) == 1             # o required
+        assert f(*ins, A, N, B, A, 2, 16, 128, 0.1, N) == 4             # o_f32 needs 16 bytes
+        assert f(*ins, A, N, A, C, 2, 16, 128, 0.1, N) == 4             # row_ml needs 8 bytes
+        assert f(*ins, A, C, A, A, 2, 16, 128, 0.0, N) == 7             # scale
+        for i in range(nin):
+            args = list(ins)
+            args[i] = N
+            assert f(*args, A, N, A, A, 2, 16, 128, 0.1, N) == 1, i
 
 
 def test_bwd_bf16_argument_errors(lib):
     f = lib.attn_bwd_bf16
     ws = ctypes.c_void_p(0x200000)
     need = lib.attn_bwd_bf16_workspace_bytes(2, 16, 128)
-    ok = [A] * 8
+    ok = [A] * 9        # q, k, v, o_f32, row_ml, dout, dq, dk, dv
     assert f(*ok, ws, need, 2, 16, 64, 0.1, N) == 3                     # d
     assert f(*ok, ws, need, 2, 1 << 23, 128, 0.1, N) == 2               # one head too long
-    for i in range(8):                                                   # every pointer is required
+    for i in range(9):                                                   # every pointer is required
         args = list(ok)
         args[i] = N
         assert f(*args, ws, need, 2, 16, 128, 0.1, N) == 1, i
     args = list(ok)
-    args[3] = ctypes.c_void_p(0x100002)                                  # lse only needs 4-byte alignment
+    args[4] = ctypes.c_void_p(0x100004)                                  # row_ml needs 8-byte alignment
     assert f(*args, ws, need, 2, 16, 128, 0.1, N) == 4
-    args[3] = ctypes.c_void_p(0x100004)
-    args[5] = B                                                          # dq misaligned
+    args[4] = B
+    args[3] = B                                                          # o_f32 misaligned
+    assert f(*args, ws, need, 2, 16, 128, 0.1, N) == 4
+    args[3] = A
+    args[6] = B                                                          # dq misaligned
     assert f(*args, ws, need, 2, 16, 128, 0.1, N) == 4
     assert f(*ok, ws, need, 2, 16, 128, 0.0, N) == 7                    # scale
     assert f(*ok, N, need, 2, 16, 128, 0.1, N) == 5                     # workspace
@@ -193,17 +215,19 @@ def test_bwd_fp4qk_argument_errors(lib):
     f = lib.attn_bwd_fp4qk
     ws = ctypes.c_void_p(0x200000)
     need = lib.attn_bwd_fp4qk_workspace_bytes(2, 16, 128)
-    ok = [A] * 10
+    ok = [A] * 11       # 4 code/scale tensors, v, o_f32, row_ml, dout, dq, dk, dv
     assert f(*ok, ws, need, 2, 16, 128, 0.1, 4, N) == 8                 # unknown flag bit
     assert f(*ok, ws, need, 2, 16, 256, 0.1, 3, N) == 3
-    for i in range(10):
+    for i in range(11):
         args = list(ok)
         args[i] = N
         assert f(*args, ws, need, 2, 16, 128, 0.1, 3, N) == 1, i
+    args = list(ok)
+    args[6] = ctypes.c_void_p(0x100004)                                  # row_ml
+    assert f(*args, ws, need, 2, 16, 128, 0.1, 3, N) == 4
     assert f(*ok, ws, need, 2, 16, 128, float("nan"), 3, N) == 7
     assert f(*ok, ws, need - 1, 2, 16, 128, 0.1, 3, N) == 5
     assert f(*ok, ctypes.c_void_p(0x200010), need, 2, 16, 128, 0.1, 3, N) == 5
-
 
 
 def test_nvfp4_buffer_sizes(lib):

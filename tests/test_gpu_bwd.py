@@ -7,9 +7,12 @@ within 2e-2 of the largest magnitude of the same tensor of the same head
 and the sums softmax fixes (sum over keys of dK is zero, of dV the sum over
 queries of dO) within 1e-2 of the summed row norms they add.
 
-The HIP forward supplies the LSE (as a training step would); the oracle
-computes the exact gradients of the same BF16 inputs (for the FP4 path, of
-the dequantized codes, with the quantizer passed straight through).  Small
+The HIP training forward supplies its fp32 O and row statistics (as a
+training step would); the oracle computes the exact gradients of the same
+BF16 inputs (for the FP4 path, of the dequantized codes, with the quantizer
+passed straight through).  The training forwards themselves are checked
+against the plain forwards: the same O and LSE bit for bit, an fp32 O that
+rounds to that O, and row statistics that give the LSE.  Small
 shapes are compared in full; the full-size workloads (40 heads x 109,000
 tokens as the benchmark times them, and 80 heads, whose last rows lie past
 2^31 bytes) on sampled dQ rows, every element of dK and dV of sampled key
@@ -93,15 +96,59 @@ def run_bwd(torch, d, dout_bits):
     from long_sequence_dense_amd import binding
     q, k, v = (bf16_dev(torch, d[n]) for n in ("q", "k", "v"))
     H, L, _ = d["q"].shape
-    o = torch.empty((H, L, 128), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((H, L), dtype=torch.float32, device="cuda")
-    binding.attn_fwd_bf16(q, k, v, o, lse, softmax_scale=d["scale"])
+    o, o32, ml = binding.attn_fwd_bf16_train(q, k, v, softmax_scale=d["scale"])
     del o
     do = bf16_dev(torch, dout_bits)
     grads = [torch.full((H, L, 128), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
-    binding.attn_bwd_bf16(q, k, v, lse, do, *grads, softmax_scale=d["scale"])
+    binding.attn_bwd_bf16(q, k, v, o32, ml, do, *grads, softmax_scale=d["scale"])
     torch.cuda.synchronize()
     return grads
+
+
+def check_train_outputs(torch, name, o_ref, lse_ref, o, lse, o32, ml):
+    """The training forward against the plain one: o and lse bit for bit, o32
+    rounds (to nearest even) to o, and (m + log2 l) ln 2 is the LSE up to the
+    fp32 roundings of the two formulas."""
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), name
+    assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32)), name
+    assert torch.equal(o32.to(torch.bfloat16).view(torch.int16), o.view(torch.int16)), name
+    m, l = ml[..., 0].double(), ml[..., 1].double()
+    assert bool((l >= 1.0).all()), name          # the row's largest weight is at least 1
+    lse2 = (m + torch.log2(l)) * np.log(2.0)
+    err = float(((lse2 - lse.double()).abs() / (1.0 + lse.double().abs())).max())
+    say("  %s: o, lse identical; o32 rounds to o; LSE from (m, l) within %.2e (relative)" % (name, err))
+    assert err <= 1e-6, name
+
+
+@pytest.mark.parametrize("cfg,H,L", [("tiny", 2, 1), ("tiny", 3, 333), ("clip15s", 2, 3000), ("fp4", 2, 4000)])
+def test_train_forward_bf16(torch, cfg, H, L):
+    from long_sequence_dense_amd import binding
+    d = inputs.make_inputs(cfg, H=H, L=L)
+    say("case train forward bf16 %s H=%d L=%d" % (cfg, H, L))
+    q, k, v = (bf16_dev(torch, d[n]) for n in ("q", "k", "v"))
+    o_ref = binding.attn_fwd_bf16(q, k, v, softmax_scale=d["scale"])
+    lse_ref = torch.empty((H, L), dtype=torch.float32, device="cuda")
+    binding.attn_fwd_bf16(q, k, v, None, lse_ref, softmax_scale=d["scale"])
+    lse = torch.empty((H, L), dtype=torch.float32, device="cuda")
+    o, o32, ml = binding.attn_fwd_bf16_train(q, k, v, None, lse, softmax_scale=d["scale"])
+    torch.cuda.synchronize()
+    check_train_outputs(torch, "bf16 %s L=%d" % (cfg, L), o_ref, lse_ref, o, lse, o32, ml)
+
+
+@pytest.mark.parametrize("cfg,H,L", [("fp4", 2, 1000), ("tiny", 1, 65)])
+def test_train_forward_fp4qk(torch, cfg, H, L):
+    from long_sequence_dense_amd import binding
+    d = inputs.make_inputs(cfg, H=H, L=L)
+    say("case train forward fp4qk %s H=%d L=%d" % (cfg, H, L))
+    q, k, v = (bf16_dev(torch, d[n]) for n in ("q", "k", "v"))
+    p = binding.qk_prep_fp4(q, k)
+    codes = (p["q_codes"], p["q_scales"], p["k_codes"], p["k_scales"])
+    lse_ref = torch.empty((H, L), dtype=torch.float32, device="cuda")
+    o_ref = binding.attn_fwd_fp4qk(*codes, v, None, lse_ref, softmax_scale=d["scale"])
+    lse = torch.empty((H, L), dtype=torch.float32, device="cuda")
+    o, o32, ml = binding.attn_fwd_fp4qk_train(*codes, v, None, lse, softmax_scale=d["scale"])
+    torch.cuda.synchronize()
+    check_train_outputs(torch, "fp4qk %s L=%d" % (cfg, L), o_ref, lse_ref, o, lse, o32, ml)
 
 
 @pytest.mark.parametrize("cfg,H,L", [("tiny", 2, 1024), ("tiny", 2, 1), ("tiny", 3, 33), ("tiny", 2, 200),
@@ -113,8 +160,31 @@ def test_bwd_small_full(torch, cfg, H, L):
     say("case bwd %s H=%d L=%d" % (cfg, H, L))
     dq, dk, dv = run_bwd(torch, d, dob)
     refs = attention_bwd_fp64(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(dob), d["scale"])
+    if L == 1:
+        check_single_key(d, dob, (dq, dk, dv), refs)
+        return
     for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
         compare("%s %s L=%d" % (name, cfg, L), to_f64(g), r)
+
+
+def check_single_key(d, dob, grads, refs):
+    """One key per head: P = 1, so dV = dO exactly and dQ = dK = 0.  The
+    computed dS = P (dP - D) is the difference of two fp32 dot products of
+    the same 128 terms dO_c V_c (O = V exactly), each within
+    gamma_128 sum_c |dO_c V_c| of the exact value (gamma_n = n u / (1 - n u),
+    u = 2^-24, the textbook bound for any summation order), so dQ and dK are
+    bounded by sigma * 2 gamma_128 sum|dO V| * max|K| (max|Q|), with a factor
+    (1 + 2^-7) for the BF16 roundings of dS and of the result."""
+    dq, dk, dv = (to_f64(g) for g in grads)
+    u = 2.0 ** -24
+    gamma = 128 * u / (1 - 128 * u)
+    do, v, q, k = f64(dob), f64(d["v"]), f64(d["q"]), f64(d["k"])
+    ds_bound = 2 * gamma * np.abs(do * v).sum(axis=2, keepdims=True)          # [H, 1, 1]
+    for name, g, x in (("dq", dq, k), ("dk", dk, q)):
+        bound = d["scale"] * ds_bound * np.abs(x).max(axis=2, keepdims=True) * (1 + 2.0 ** -7)
+        say("  %s single key: max |%s| %.3e, bound %.3e" % (name, name, float(np.abs(g).max()), float(bound.min())))
+        assert np.all(np.abs(g) <= bound), name
+    assert np.array_equal(dv, refs[2]), "dv single key"
 
 
 def test_bwd_mid_full(torch):
@@ -133,7 +203,8 @@ def test_bwd_mid_full(torch):
 def test_bwd_peaked_rows_full(torch):
     """The FP4 workload's structure (Student-t(3) with x20 channels) at
     H = 2, L = 4000: many rows put nearly all their weight on one key, so dS
-    is nearly zero there and only a D formed consistently with P keeps the
+    is nearly zero there and only a D formed with the weights of P (from the
+    forward's fp32 O, not its BF16 O) keeps the
     gradient's relative accuracy."""
     from oracle.attention_bwd import attention_bwd_fp64
     d = inputs.make_inputs("fp4", H=2, L=4000)
@@ -227,15 +298,12 @@ def run_fp4_bwd(torch, d, dout_bits, flags):
     q, k, v = (bf16_dev(torch, d[n]) for n in ("q", "k", "v"))
     H, L, _ = d["q"].shape
     prep = binding.qk_prep_fp4_ex(q, k, flags)
-    o = torch.empty((H, L, 128), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((H, L), dtype=torch.float32, device="cuda")
-    binding.attn_fwd_fp4qk(prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], v, o, lse,
-                           softmax_scale=d["scale"])
+    codes = (prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"])
+    o, o32, ml = binding.attn_fwd_fp4qk_train(*codes, v, softmax_scale=d["scale"])
     del o
     do = bf16_dev(torch, dout_bits)
     grads = [torch.full((H, L, 128), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
-    binding.attn_bwd_fp4qk(prep["q_codes"], prep["q_scales"], prep["k_codes"], prep["k_scales"], v, lse, do,
-                           *grads, softmax_scale=d["scale"], flags=flags)
+    binding.attn_bwd_fp4qk(*codes, v, o32, ml, do, *grads, softmax_scale=d["scale"], flags=flags)
     torch.cuda.synchronize()
     return grads, prep
 
