@@ -19,10 +19,12 @@
 //     index - and V^T is read from the row-major V tile with the gfx950 LDS
 //     transpose read (ds_read_b64_tr_b16), addressed to reproduce that
 //     permutation.
-//   * Software pipeline, per iteration t: the MFMAs of P(t-1) V(t-1) and of
-//     K(t+1) Q^T are issued while the VALU computes the softmax of tile t, so
-//     the matrix cores and the vector ALU work at the same time inside each
-//     wave.  K runs two tiles ahead of the P.V stage, V one tile.
+//   * Software pipeline, per iteration t: the MFMAs of P(t-1) V(t-1) are
+//     issued in fenced slots, each followed by two exponentials of tile t
+//     and by the V reads of the MFMA four slots later, so the matrix core and
+//     the vector ALU work at the same time inside each wave and no MFMA waits
+//     on a fresh LDS read; then K(t+1) Q^T.  K runs two tiles ahead of the
+//     P.V stage, V one tile.
 //   * K and V tiles are double-buffered in LDS with padded rows (bank-conflict
 //     free operand reads at immediate offsets) and prefetched through
 //     registers one iteration ahead.  One barrier per tile.
@@ -234,21 +236,8 @@ struct Ctx {
 };
 
 // Masks for the scheduling groups: VALU 0x2, MFMA 0x8, VMEM read 0x20,
-// DS read 0x100, DS write 0x200.
-// V operand reads run four MFMAs ahead of their MFMA; the first KPRE K
-// operands of the next tile are read during the last four P.V MFMAs, so the
-// score MFMAs start with KPRE operands in registers and keep reading KPRE
-// ahead.
-__device__ __forceinline__ void schedule_pv_half(bool kpre) {
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    else if (kpre) __builtin_amdgcn_sched_group_barrier(0x100, KPRE / 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-  }
-}
+// DS read 0x100, DS write 0x200.  The score MFMAs start with KPRE operands
+// in registers (read during the P.V half) and keep reading KPRE ahead.
 __device__ __forceinline__ void schedule_qk_half() {
   if (KPRE < 4) __builtin_amdgcn_sched_group_barrier(0x100, 4 - KPRE, 0);
   constexpr int AHEAD = KPRE < 4 ? 4 : KPRE;
@@ -283,10 +272,60 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float c, float n
   return lsum;
 }
 
+// The first half of a pipeline iteration as 16 fenced slots: slot i issues
+// the V transpose reads of P.V MFMA i + 4, the MFMA i (channel block i % 4,
+// key chunk i / 4), and two of the tile's exponentials; every fourth slot
+// rounds the eight exponentials just taken to BF16 and adds them to the row
+// sum.  The exponentials, their rounding and the order of the sum are those
+// of exp_tile.  With the operands read four MFMAs ahead, no MFMA waits on a
+// fresh LDS read, and the VALU work issues while the matrix core runs.  The
+// last four slots also read the first KPRE K operands of the next tile.
+template <bool KP>
+__device__ __forceinline__ float pv_exp_tile(const uint16_t* vl, const bf16x8 (&pb)[4], f32x16 (&oacc)[4],
+                                             const f32x16 (&s)[2], float c, float negm, bf16x8 (&p)[4],
+                                             const uint16_t* kl, bf16x8 (&kpre)[KPRE]) {
+  constexpr int AHEAD = 4;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8 va[16];
+  auto vread = [&](int i) {
+    const uint16_t* a0 = vl + 16 * (i >> 2) * VS + 32 * (i & 3);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u16*)a0);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u16*)(a0 + 8 * VS));
+    va[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) vread(i);
+  __builtin_amdgcn_sched_barrier(0);
+  float lsum = 0.0f;
+  f32x8 pf;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + AHEAD < 16) vread(i + AHEAD);
+    if constexpr (KP) {
+      if (i >= 16 - KPRE) kpre[i - (16 - KPRE)] = k_operand(kl, i - (16 - KPRE));
+    }
+    oacc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[i >> 2], oacc[i & 3], 0, 0, 0);
+    const int g = i >> 2;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int k = 2 * (i & 3) + e;
+      pf[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g >> 1][8 * (g & 1) + k], c, negm));
+    }
+    if ((i & 3) == 3) {
+      p[g] = __builtin_convertvector(pf, bf16x8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[g][2 * j], p[g][2 * j + 1]}, ones, lsum, false);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return lsum;
+}
+
 // One pipeline iteration t.  First half: P(t-1) V(t-1) on the matrix cores
-// while the VALU exponentiates tile t.  Second half: S(t+1) = K(t+1) Q^T on
-// the matrix cores (into the registers the exponentials just freed) while the
-// VALU finishes the row sums; then V(t) and K(t+2) are staged into LDS.
+// while the VALU exponentiates tile t (pv_exp_tile).  Second half:
+// S(t+1) = K(t+1) Q^T on the matrix cores, into the registers the
+// exponentials just freed; then V(t) and K(t+2) are staged into LDS.
 template <bool FP4, bool FIRST, bool NEXT, bool NEXT2, bool LAST>
 __device__ __forceinline__ void step(Smem& sm, WaveState& st, const Ctx& cx, int t) {
   const int kv0 = t * BC;
@@ -300,7 +339,6 @@ __device__ __forceinline__ void step(Smem& sm, WaveState& st, const Ctx& cx, int
   if constexpr (NEXT2) load_k<FP4>(cx.hb, kv0 + 2 * BC, cx.tid, kr);
 
   // ---- first half ----
-  if constexpr (!FIRST) pv_tile(sm.v[(t - 1) & 1] + cx.v_lane, st.p_prev, st.oacc);
   if constexpr (LAST) {
     if (kv0 + BC > cx.L) {
 #pragma unroll
@@ -314,13 +352,18 @@ __device__ __forceinline__ void step(Smem& sm, WaveState& st, const Ctx& cx, int
   // sum could overflow (above 2^16, infinite on the first tile) is redone
   // below against its true max.
   bf16x8 p_cur[4];
-  float lsum = exp_tile(st.s, cx.c, -st.m_used, p_cur);
   bf16x8 kpre[KPRE];
-  if constexpr (NEXT) {
+  float lsum;
+  if constexpr (!FIRST) {
+    lsum = pv_exp_tile<NEXT>(sm.v[(t - 1) & 1] + cx.v_lane, st.p_prev, st.oacc, st.s, cx.c, -st.m_used, p_cur,
+                             sm.k[(t + 1) & 1] + cx.k_lane, kpre);
+  } else {
+    lsum = exp_tile(st.s, cx.c, -st.m_used, p_cur);
+    if constexpr (NEXT) {
 #pragma unroll
-    for (int i = 0; i < KPRE; ++i) kpre[i] = k_operand(sm.k[(t + 1) & 1] + cx.k_lane, i);
+      for (int i = 0; i < KPRE; ++i) kpre[i] = k_operand(sm.k[(t + 1) & 1] + cx.k_lane, i);
+    }
   }
-  if constexpr (!FIRST) schedule_pv_half(NEXT);
 
   // ---- rare path: recompute the tile against its true max ----
   st.rescale = __builtin_amdgcn_ballot_w64(!(lsum <= kSumBound)) != 0;
