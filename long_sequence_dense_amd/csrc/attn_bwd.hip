@@ -57,9 +57,20 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr float kLog2eF = 1.44269504088896340736f;
-constexpr int TS = kHeadDim + 32;       // LDS row stride (bf16) of the streamed tiles: 320 B
+constexpr int TS = kHeadDim;            // LDS row of the streamed tiles: 256 B, 16-byte chunks swizzled
 constexpr int TR = 32;                  // rows per streamed tile
 constexpr int TILE = TR * TS;           // one tile in LDS (bf16 elements)
+
+// The streamed tiles are read both as MFMA row operands (a quarter-wave reads
+// one 16-byte chunk of 16 consecutive rows) and by the transpose reads (a
+// half-wave reads 8-byte pieces of 64 bytes of 4 consecutive rows from a
+// multiple of 4).  No row padding keeps both free of LDS bank conflicts (64
+// banks of 4 bytes): padding that spreads 16 rows over the banks overlaps
+// 4 rows' 64-byte pieces, and the converse.  So chunk c of row r is stored at
+// chunk c ^ swz(r): swz takes 16 distinct values on any 16 consecutive rows,
+// and on 4 consecutive rows from a multiple of 4 its high bits move each
+// row's 64-byte piece to a different quarter of the banks.
+__device__ __forceinline__ int swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -96,20 +107,48 @@ __device__ __forceinline__ void dma_dword(const Rsrc& r, const void* lds_dst, in
 }
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
+// Per-lane LDS offsets (bf16 elements) of the swizzled tile reads.
+struct Lanes {
+  int lane, l32, hf;
+  int row[8];         // row operand, channel chunk kk: row l % 32, channels 16 kk + 8 (l / 32) .. +7
+  int tr[8];          // transpose read [2 db + h]: tile rows 4 (l / 32) + (l % 16) / 4 + 8 h,
+                      // channels 32 db + 16 ((l / 16) % 2) + 4 (l % 4) .. +3
+};
+
+__device__ __forceinline__ Lanes lanes(int tid) {
+  Lanes x;
+  x.lane = tid & 63;
+  x.l32 = x.lane & 31;
+  x.hf = x.lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) x.row[kk] = x.l32 * TS + 8 * ((2 * kk + x.hf) ^ swz(x.l32));
+  const int r16 = x.lane & 15;
+  const int r0 = 4 * x.hf + (r16 >> 2);
+  const int c1 = 2 * ((x.lane >> 4) & 1) + ((r16 & 3) >> 1);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = r0 + 8 * h;
+      x.tr[2 * db + h] = r * TS + 8 * ((4 * db + c1) ^ swz(r)) + 4 * (r16 & 1);
+    }
+  return x;
+}
+
 // A operand from rows of a row-major LDS tile: lane l reads row l % 32,
-// channels 16 * kk + 8 * (l / 32) .. +7.  `lane_row` = (l % 32) * TS + 8 * (l / 32).
-__device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int lane_row, int kk) {
-  return __builtin_bit_cast(bf16x8, *(const u16x8*)(tile + lane_row + 16 * kk));
+// channels 16 * kk + 8 * (l / 32) .. +7.
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, const Lanes& ln, int kk) {
+  return __builtin_bit_cast(bf16x8, *(const u16x8*)(tile + ln.row[kk]));
 }
 
 // A operand X^T from a row-major LDS tile X[row][channel]: rows of the
 // operand are channels 32 * db .. +31, its k index runs over tile rows
-// 16 * cc .. +15 in the order of the accumulator-derived B operands.
-// `lane_tr` = (4 * (l / 32) + (l % 16) / 4) * TS + 16 * ((l / 16) % 2) + 4 * (l % 4).
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int lane_tr, int cc, int db) {
-  const uint16_t* a0 = tile + lane_tr + 16 * cc * TS + 32 * db;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u16*)a0);
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u16*)(a0 + 8 * TS));
+// 16 * cc .. +15 in the order of the accumulator-derived B operands (row
+// 16 cc + r has the swizzle of row r: swz depends on r mod 16 only).
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, const Lanes& ln, int cc, int db) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u16*)(tile + ln.tr[2 * db] + 16 * cc * TS));
+  const v4i16 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u16*)(tile + ln.tr[2 * db + 1] + 16 * cc * TS));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -139,24 +178,9 @@ __device__ __forceinline__ void store_rows(uint16_t* tile, int tid, const RowSta
 #pragma unroll
   for (int i = 0; i < RowStage<NT>::N; ++i) {
     const int id = tid + NT * i;
-    *(u32x4*)(tile + (id >> 4) * TS + (id & 15) * 8) = s.c[i];
+    const int r = id >> 4;
+    *(u32x4*)(tile + r * TS + 8 * ((id & 15) ^ swz(r))) = s.c[i];
   }
-}
-
-// Lane address parts shared by the two main kernels.
-struct Lanes {
-  int lane, l32, hf, lane_row, lane_tr;
-};
-
-__device__ __forceinline__ Lanes lanes(int tid) {
-  Lanes x;
-  x.lane = tid & 63;
-  x.l32 = x.lane & 31;
-  x.hf = x.lane >> 5;
-  const int r16 = x.lane & 15;
-  x.lane_row = x.l32 * TS + 8 * x.hf;
-  x.lane_tr = (4 * x.hf + (r16 >> 2)) * TS + 16 * ((x.lane >> 4) & 1) + 4 * (r16 & 3);
-  return x;
 }
 
 // Logical workgroup id with each XCD (hardware id % 8) given a contiguous
@@ -253,8 +277,9 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
   auto stage = [&](int q0, int buf) {
 #pragma unroll
     for (int i = 0; i < TR / DKDV_WAVES; ++i) {
+      // lane j fills dword j of LDS row r: dword j % 4 of logical chunk (j / 4) ^ swz(r)
       const int r = wave_u * (TR / DKDV_WAVES) + i;
-      const int voff = (q0 + r) * (kHeadDim * 2) + 4 * ln.lane;
+      const int voff = (q0 + r) * (kHeadDim * 2) + 16 * ((ln.lane >> 2) ^ swz(r)) + 4 * (ln.lane & 3);
       dma_dword(rq, sm.q[buf] + r * TS, voff);
       dma_dword(rdo, sm.dout[buf] + r * TS, voff);
     }
@@ -277,10 +302,10 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
     // S = Q K^T and dP = dO V^T for this wave's keys: rows = queries.
     f32x16 s = (f32x16)0.0f, dp = (f32x16)0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s = mfma(row_operand(qt, ln.lane_row, kk), kreg[kk], s);
+    for (int kk = 0; kk < 8; ++kk) s = mfma(row_operand(qt, ln, kk), kreg[kk], s);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
-      dp = mfma(row_operand(dt, ln.lane_row, kk), __builtin_bit_cast(bf16x8, *(const u16x8*)(sm.v + v_lane + 16 * kk)),
+      dp = mfma(row_operand(dt, ln, kk), __builtin_bit_cast(bf16x8, *(const u16x8*)(sm.v + v_lane + 16 * kk)),
                 dp);
     // P = exp2(S c - m) / l and dS = P (dP - D); accumulator element i is
     // query row 8 * (i / 4) + 4 * hf + i % 4 of the tile.
@@ -308,11 +333,11 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) dvacc[db] = mfma(tr_operand(dt, ln.lane_tr, cc, db), pb[cc], dvacc[db]);
+      for (int db = 0; db < 4; ++db) dvacc[db] = mfma(tr_operand(dt, ln, cc, db), pb[cc], dvacc[db]);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) dkacc[db] = mfma(tr_operand(qt, ln.lane_tr, cc, db), dsb[cc], dkacc[db]);
+      for (int db = 0; db < 4; ++db) dkacc[db] = mfma(tr_operand(qt, ln, cc, db), dsb[cc], dkacc[db]);
 
     dma_wait();
     __syncthreads();
@@ -430,9 +455,9 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
     // of the tile.  Keys past L are zero rows.
     f32x16 s = (f32x16)0.0f, dp = (f32x16)0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s = mfma(row_operand(kt, ln.lane_row, kk), qreg[kk], s);
+    for (int kk = 0; kk < 8; ++kk) s = mfma(row_operand(kt, ln, kk), qreg[kk], s);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) dp = mfma(row_operand(vt, ln.lane_row, kk), doreg[kk], dp);
+    for (int kk = 0; kk < 8; ++kk) dp = mfma(row_operand(vt, ln, kk), doreg[kk], dp);
     f32x8 df[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -446,7 +471,7 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) dqacc[db] = mfma(tr_operand(kt, ln.lane_tr, cc, db), dsb[cc], dqacc[db]);
+      for (int db = 0; db < 4; ++db) dqacc[db] = mfma(tr_operand(kt, ln, cc, db), dsb[cc], dqacc[db]);
 
     if (more) {
       store_rows(sm.k[buf ^ 1], tid, sk);
