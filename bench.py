@@ -7,8 +7,14 @@ clip scale (H = 40 heads, L = 109,000 tokens, d = 128):
   same outliers, N(0,1) V).
 value = attention FLOP of the step (2 x 4 H L^2 d) / step time, TFLOP/s.
 Prints ONE JSON line (rank 0).  Inputs are resident in HBM before timing.
+After the timed steps (outside them) the line also carries the extra paths
+(fused-Q FP4, the backward, the NVFP4 linear, the other configurations), the
+CPU oracle baseline and the standalone matrix-core probe's sustained BF16 MFMA
+rate for random and all-zero operands (the attainable ceiling under this GPU's
+power limit, against which roofline.achieved is also read).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-mfma-ceiling] [--mfma-ceiling]
 """
 
 import argparse
@@ -256,6 +262,10 @@ def main():
     ap.add_argument("--steps", type=int, default=8)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the standalone MFMA ceiling probe (random vs zero operands) after the timed steps")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the standalone MFMA ceiling probe and print its JSON line")
     ap.add_argument("--only", choices=["all", "bf16"], default="all",
                     help="bf16: time only attn_fwd_bf16 (for profiling runs)")
     ap.add_argument("--no-bwd", action="store_true",
@@ -276,6 +286,10 @@ def main():
               "(attention would shard by head with no exchange); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.mfma_ceiling:
+        print(json.dumps(mfma_ceiling()), flush=True)
+        return
 
     import torch
     from long_sequence_dense_amd import binding
@@ -506,7 +520,29 @@ def main():
             par = res["cpu_baseline"].pop("parity")
             for key, val in par.items():
                 res["paths"][key]["parity_vs_oracle"] = val
+    if not args.no_mfma_ceiling:
+        ceil = mfma_ceiling()
+        if ceil is not None:
+            rnd = ceil["mfma_ceiling_bf16_TFLOP/s"]["random_operands"]
+            ceil["attn_fwd_bf16_frac_of_random_operand_ceiling"] = round(res["roofline"]["achieved"] / rnd, 4)
+        res["mfma_ceiling_probe"] = ceil
     print(json.dumps(res), flush=True)
+
+
+def mfma_ceiling():
+    """Run the standalone matrix-core probe (built in-tree by the library's
+    build step): the dense BF16 MFMA rate this GPU sustains with nothing else
+    running, for random and for all-zero operands.  None if it is not built."""
+    import subprocess
+    exe = os.path.join(ROOT, "long_sequence_dense_amd", "mfma_ceiling_probe")
+    if not os.path.exists(exe):
+        log("mfma_ceiling_probe not built; skipped")
+        return None
+    log("running the MFMA ceiling probe ...")
+    r = subprocess.run([exe], stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+    if r.returncode != 0:
+        raise RuntimeError("mfma_ceiling_probe failed (%d): %s" % (r.returncode, r.stderr.strip()))
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 if __name__ == "__main__":

@@ -1,7 +1,8 @@
 """Build liblsd_attn.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
 
 Usage: python -m long_sequence_dense_amd.build   (or build() from Python).
-Every call recompiles.  Output: long_sequence_dense_amd/liblsd_attn.so
+Every call recompiles.  Output: long_sequence_dense_amd/liblsd_attn.so and the
+standalone matrix-core ceiling probe long_sequence_dense_amd/mfma_ceiling_probe.
 """
 
 import os
@@ -12,6 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblsd_attn.so")
+PROBE = os.path.join(HERE, "mfma_ceiling_probe")
 ARCH = "gfx950"
 
 COMMON = [
@@ -61,6 +63,10 @@ def build(verbose=False):
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
     os.replace(tmp, LIB)
+    # the matrix-core ceiling probe (a standalone executable, not part of the library)
+    tmp = PROBE + ".tmp"
+    _run([cc] + COMMON + ["-o", tmp, os.path.join(CSRC, "mfma_ceiling_probe.hip")])
+    os.replace(tmp, PROBE)
     return LIB
 
 
