@@ -360,6 +360,16 @@ def main():
         wc, ws_ = binding.nvfp4_quantize(w, gw, layout=T, stream=stream)
         binding.nvfp4_linear(xc, xs, gx, wc, ws_, gw, stream=stream, layout=T, M=LIN_M, N=LIN_N, K=LIN_K)
         torch.cuda.synchronize()
+        del x, w, xc, xs, wc, ws_
+        # one training forward and backward of the BF16 path
+        o32 = torch.empty((H, L, d), dtype=torch.float32, device=dev)
+        ml = torch.empty((H, L, 2), dtype=torch.float32, device=dev)
+        binding.attn_fwd_bf16_train(x4["q"], x4["k"], x4["v"], o4, None, o32, ml, cfg4.scale, stream)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5)
+        dout = torch.randn((H, L, d), dtype=torch.float32, device=dev, generator=gen).to(torch.bfloat16)
+        binding.attn_bwd_bf16(x4["q"], x4["k"], x4["v"], o32, ml, dout, softmax_scale=cfg4.scale, stream=stream)
+        torch.cuda.synchronize()
         log("pmc probe done")
         return
 
