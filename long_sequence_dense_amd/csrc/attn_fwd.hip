@@ -322,6 +322,57 @@ __device__ __forceinline__ float pv_exp_tile(const uint16_t* vl, const bf16x8 (&
   return lsum;
 }
 
+// The second half of a pipeline iteration as 16 fenced slots: slot j issues
+// the K read of score MFMA j + KPRE and the score MFMA j (key block j / 8,
+// channel chunk j % 8), the first KPRE operands coming from kpre; with STORE
+// the slots also stage K(t+2) into LDS (its global loads were issued at the
+// start of the iteration): the exact dequantization of this thread's FP4
+// 16-value block, one pair of values per slot in slots 0-7, its two 16-byte
+// stores in slots 8 and 9 (otherwise a VALU-only stretch after the score
+// MFMAs).  The arithmetic and the store addresses are those of store_k.
+template <bool FP4, bool STORE>
+__device__ __forceinline__ void qk_stage_tile(const uint16_t* kl, const bf16x8 (&kpre)[KPRE], const bf16x8 (&qreg)[8],
+                                              f32x16 (&s)[2], uint16_t* kb, int tid, const KPrefetch& kr) {
+  static_assert(FP4 && NLD4 == 1, "FP4 staging: one 16-value block of K per thread and tile");
+  bf16x8 ka[16];
+#pragma unroll
+  for (int i = 0; i < KPRE; ++i) ka[i] = kpre[i];
+  s[0] = (f32x16)0.0f;
+  s[1] = (f32x16)0.0f;
+  float f[16];
+  float sc = 0.0f;
+  if constexpr (FP4 && STORE) sc = e4m3_to_f32(kr.scale[0] & 0xFF);
+  const int key = tid >> 3, blk = tid & 7;       // FP4 staging: this thread's block
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j + KPRE < 16) ka[j + KPRE] = k_operand(kl, j + KPRE);
+    s[j >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qreg[j & 7], s[j >> 3], 0, 0, 0);
+    if constexpr (STORE) {
+      if constexpr (FP4) {
+        if (j < 8) {
+          const uint32_t w = kr.codes[0][j >> 2];
+          float lo = 0.0f, hi = 0.0f;
+          switch (j & 3) {                       // the byte select must be a constant
+            case 0: { const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); lo = a[0]; hi = a[1]; break; }
+            case 1: { const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); lo = a[0]; hi = a[1]; break; }
+            case 2: { const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); lo = a[0]; hi = a[1]; break; }
+            default: { const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); lo = a[0]; hi = a[1]; break; }
+          }
+          f[2 * j] = lo * sc;
+          f[2 * j + 1] = hi * sc;
+        } else if (j < 10) {
+          const int h = j - 8;
+          u16x8 r;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) r[e] = (uint16_t)(__float_as_uint(f[8 * h + e]) >> 16);
+          *(u16x8*)(kb + key * KS + 16 * blk + 8 * h) = r;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One pipeline iteration t.  First half: P(t-1) V(t-1) on the matrix cores
 // while the VALU exponentiates tile t (pv_exp_tile).  Second half:
 // S(t+1) = K(t+1) Q^T on the matrix cores, into the registers the
@@ -384,12 +435,19 @@ __device__ __forceinline__ void step(Smem& sm, WaveState& st, const Ctx& cx, int
   st.l_run += lsum;
 
   // ---- second half ----
-  if constexpr (NEXT) qk_tile<KPRE>(sm.k[(t + 1) & 1] + cx.k_lane, kpre, st.qreg, st.s);
-  if constexpr (NEXT) schedule_qk_half();
+  // (K(t+2) goes to K(t)'s buffer: no wave reads K(t) after the last
+  // barrier).  The FP4 path dequantizes it in the score slots; the BF16 path
+  // stores it after them.
+  if constexpr (NEXT && FP4) {
+    qk_stage_tile<true, NEXT2>(sm.k[(t + 1) & 1] + cx.k_lane, kpre, st.qreg, st.s, sm.k[t & 1], cx.tid, kr);
+  } else if constexpr (NEXT) {
+    qk_tile<KPRE>(sm.k[(t + 1) & 1] + cx.k_lane, kpre, st.qreg, st.s);
+    schedule_qk_half();
+  }
 
   // ---- stage the prefetched tiles, then one barrier ----
   store_v(sm.v[t & 1], cx.tid, vr);
-  if constexpr (NEXT2) store_k<FP4>(sm.k[t & 1], cx.tid, kr);
+  if constexpr (NEXT2 && !FP4) store_k<false>(sm.k[t & 1], cx.tid, kr);
   __syncthreads();
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) st.p_prev[cc] = p_cur[cc];
