@@ -308,36 +308,67 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
       dp = mfma(row_operand(dt, ln, kk), __builtin_bit_cast(bf16x8, *(const u16x8*)(sm.v + v_lane + 16 * kk)),
                 dp);
     // P = exp2(S c - m) / l and dS = P (dP - D); accumulator element i is
-    // query row 8 * (i / 4) + 4 * hf + i % 4 of the tile.
+    // query row 8 * (i / 4) + 4 * hf + i % 4 of the tile.  Then dV^T += dO^T P
+    // and dK^T += Q^T dS (16-query chunks cc, channel blocks db) as 16 fenced
+    // slots, each with the transpose reads of the MFMA two slots later and a
+    // share of the VALU work the later slots need: P of chunk 0 first, P of
+    // chunk 1 during the chunk-0 dV MFMAs, dS of chunk 0 during the chunk-1
+    // dV MFMAs, dS of chunk 1 during the chunk-0 dK MFMAs.  The products
+    // accumulate in the same order as chunk by chunk.
+    const float* st_m = sm.m2[buf];
+    const float* st_i = sm.invl[buf];
+    const float* st_d = sm.dsum[buf];
+    auto stat = [&](const float* a, int g) { return *(const f32x4*)(a + 8 * g + 4 * ln.hf); };
     f32x8 pf[2], df[2];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 m4 = *(const f32x4*)(&sm.m2[buf][8 * g + 4 * ln.hf]);
-      const f32x4 i4 = *(const f32x4*)(&sm.invl[buf][8 * g + 4 * ln.hf]);
-      const f32x4 d4 = *(const f32x4*)(&sm.dsum[buf][8 * g + 4 * ln.hf]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * g + j;
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m4[j])) * i4[j];
-        pf[i >> 3][i & 7] = pv;
-        df[i >> 3][i & 7] = pv * (dp[i] - d4[j]);
-      }
-    }
     bf16x8 pb[2], dsb[2];
+    auto p_val = [&](int i, const f32x4& m4, const f32x4& i4) {
+      pf[i >> 3][i & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m4[i & 3])) * i4[i & 3];
+    };
+    auto ds_val = [&](int i, const f32x4& d4) { df[i >> 3][i & 7] = pf[i >> 3][i & 7] * (dp[i] - d4[i & 3]); };
+    {
+      const f32x4 m0 = stat(st_m, 0), i0 = stat(st_i, 0), m1 = stat(st_m, 1), i1 = stat(st_i, 1);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      pb[cc] = __builtin_convertvector(pf[cc], bf16x8);
-      dsb[cc] = __builtin_convertvector(df[cc], bf16x8);
+      for (int i = 0; i < 4; ++i) p_val(i, m0, i0);
+#pragma unroll
+      for (int i = 4; i < 8; ++i) p_val(i, m1, i1);
+      pb[0] = __builtin_convertvector(pf[0], bf16x8);
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (channel blocks db, 16-query chunks cc).
+    f32x4 mc = stat(st_m, 2), ic = stat(st_i, 2), dc;
+    auto opnd = [&](int k) {
+      return k < 8 ? tr_operand(dt, ln, k >> 2, k & 3) : tr_operand(qt, ln, (k - 8) >> 2, (k - 8) & 3);
+    };
+    constexpr int AH = 2;
+    bf16x8 va[16];
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+    for (int k = 0; k < AH; ++k) va[k] = opnd(k);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) dvacc[db] = mfma(tr_operand(dt, ln, cc, db), pb[cc], dvacc[db]);
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) dkacc[db] = mfma(tr_operand(qt, ln, cc, db), dsb[cc], dkacc[db]);
+    for (int k = 0; k < 16; ++k) {
+      if (k + AH < 16) va[k + AH] = opnd(k + AH);
+      if (k < 8)
+        dvacc[k & 3] = mfma(va[k], pb[k >> 2], dvacc[k & 3]);
+      else
+        dkacc[k & 3] = mfma(va[k], dsb[(k - 8) >> 2], dkacc[k & 3]);
+      if (k < 4) {                                // P of chunk 1: rows of stat groups 2, 3
+        p_val(8 + 2 * k, mc, ic);
+        p_val(9 + 2 * k, mc, ic);
+        if (k == 1) {
+          mc = stat(st_m, 3);
+          ic = stat(st_i, 3);
+        }
+        if (k == 3) {
+          pb[1] = __builtin_convertvector(pf[1], bf16x8);
+          dc = stat(st_d, 0);
+        }
+      } else if (k < 12) {                        // dS of chunk 0, then of chunk 1: groups (k - 4) / 2
+        ds_val(2 * (k - 4), dc);
+        ds_val(2 * (k - 4) + 1, dc);
+        if ((k & 1) && k < 11) dc = stat(st_d, (k - 3) >> 1);
+        if (k == 7) dsb[0] = __builtin_convertvector(df[0], bf16x8);
+        if (k == 11) dsb[1] = __builtin_convertvector(df[1], bf16x8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     dma_wait();
     __syncthreads();
