@@ -11,7 +11,12 @@ After the timed steps (outside them) the line also carries the extra paths
 (fused-Q FP4, the backward, the NVFP4 linear, the other configurations), the
 CPU oracle baseline and the standalone matrix-core probe's sustained BF16 MFMA
 rate for random and all-zero operands (the attainable ceiling under this GPU's
-power limit, against which roofline.achieved is also read).
+power limit, against which roofline.achieved is also read).  The shader
+clock is sampled with amd-smi while the timed steps run.  The step's prep
+follows the BF16 launch, which streams 2.2 GB of other tensors through the
+256 MB memory-side cache, so it starts cold; the separately timed
+memory-bound calls (K-only prep, NVFP4 quantizer) are each preceded by a
+512 MB write that evicts that cache, outside the timed interval.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-mfma-ceiling] [--mfma-ceiling]
@@ -178,9 +183,14 @@ def linear_operands(torch, dev):
     return x, w, gx, gw
 
 
-def time_calls(torch, stream, fn, n=3):
+def time_calls(torch, stream, fn, n=3, before=None):
+    """One warm-up and n timed calls of fn on the launch stream (HIP events);
+    `before`, if given, runs on the stream ahead of each call, outside the
+    timed interval."""
     times = []
     for i in range(n + 1):
+        if before is not None:
+            before()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -192,6 +202,67 @@ def time_calls(torch, stream, fn, n=3):
     return sum(times) / len(times)
 
 
+class MallFlush:
+    """A 512 MB write on the launch stream: evicts the 256 MB memory-side
+    cache, so that a separately timed memory-bound call cannot read its inputs
+    from it warm from the previous call."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(self.i & 0xFF)
+
+
+class ClockSampler:
+    """Samples the GPU's shader clock with `amd-smi metric -c` (the mean of
+    the eight XCD clocks per sample) from a background thread while the timed
+    steps run."""
+
+    def __init__(self, interval=0.25):
+        import threading
+        self.interval = interval
+        self.samples = []
+        self.error = None
+        self.stop_event = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _one(self):
+        import subprocess
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], stdout=subprocess.PIPE,
+                           stderr=subprocess.PIPE, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        clocks = d["gpu_data"][0]["clock"]
+        vals = [float(v["clk"]["value"]) for k, v in clocks.items() if k.startswith("gfx_")]
+        return sum(vals) / len(vals)
+
+    def _run(self):
+        while not self.stop_event.is_set():
+            try:
+                self.samples.append(self._one())
+            except Exception as e:          # no amd-smi, other output: report the reason
+                self.error = "%s: %s" % (type(e).__name__, e)
+                return
+            self.stop_event.wait(self.interval)
+
+    def start(self):
+        self.thread.start()
+        return self
+
+    def stop(self):
+        self.stop_event.set()
+        self.thread.join(timeout=30)
+        if not self.samples:
+            return {"error": self.error or "no sample"}
+        xs = self.samples
+        return {"source": "amd-smi metric -c, mean of the 8 XCD shader clocks per sample",
+                "window": "the timed steps (both attention launches and the prep)",
+                "samples": len(xs), "mean_mhz": round(sum(xs) / len(xs), 1),
+                "min_mhz": round(min(xs), 1), "max_mhz": round(max(xs), 1)}
+
+
 def linear_path(torch, binding, stream, dev):
     x, w, gx, gw = linear_operands(torch, dev)
     M, N, K = LIN_M, LIN_N, LIN_K
@@ -199,7 +270,10 @@ def linear_path(torch, binding, stream, dev):
     xc, xs = binding.nvfp4_quantize(x, gx, layout=T, stream=stream)
     wc, ws = binding.nvfp4_quantize(w, gw, layout=T, stream=stream)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    t_q = time_calls(torch, stream, lambda: binding.nvfp4_quantize(x, gx, xc, xs, layout=T, stream=stream))
+    flush = MallFlush(torch, dev)
+    t_q = time_calls(torch, stream, lambda: binding.nvfp4_quantize(x, gx, xc, xs, layout=T, stream=stream),
+                     before=flush)
+    del flush
     t_l = time_calls(torch, stream, lambda: binding.nvfp4_linear(xc, xs, gx, wc, ws, gw, y, stream=stream,
                                                                  layout=T, M=M, N=N, K=K))
     assert not torch.isnan(y).any().item()
@@ -378,11 +452,13 @@ def main():
         step(False)
     torch.cuda.synchronize()
     log("timing %d steps ..." % args.steps)
+    sampler = ClockSampler().start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk = sampler.stop()
     log("timed region %.2f s" % wall)
     assert not torch.isnan(o4).any().item() and not torch.isnan(o5).any().item()
 
@@ -415,7 +491,10 @@ def main():
         log("timing the fused-Q FP4 path (3 calls) ...")
         kflags = binding.PREP_SMOOTH_K | binding.PREP_ROTATE | binding.PREP_K_ONLY
         kprep = {key: prep[key] for key in ("k_codes", "k_scales", "k_mean")}
-        t_kp = time_calls(torch, stream, lambda: binding.qk_prep_fp4_ex(None, x5["k"], kflags, kprep, ws, stream))
+        flush = MallFlush(torch, dev)
+        t_kp = time_calls(torch, stream, lambda: binding.qk_prep_fp4_ex(None, x5["k"], kflags, kprep, ws, stream),
+                          before=flush)
+        del flush
         o5f = torch.empty_like(o5)
         t_fq = time_calls(torch, stream, lambda: binding.attn_fwd_fp4qk_fused_q(
             x5["q"], kprep["k_codes"], kprep["k_scales"], x5["v"], o5f, None, cfg5.scale, stream))
@@ -513,6 +592,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flop_per_launch": fl},
         "paths": paths,
+        "sclk_during_timed_steps": sclk,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
