@@ -253,7 +253,11 @@ class ClockSampler:
 
     def stop(self):
         self.stop_event.set()
-        self.thread.join(timeout=30)
+        if self.thread.is_alive():
+            self.thread.join(timeout=30)
+        return self.summary()
+
+    def summary(self):
         if not self.samples:
             return {"error": self.error or "no sample"}
         xs = self.samples

@@ -55,3 +55,42 @@ def test_traffic_is_reported_only_for_the_measured_source():
         assert bench.stored_traffic() == rec["hbm_bytes_per_launch"] > 0
     else:
         assert bench.stored_traffic() is None
+
+
+def _smi_json(mhz):
+    # the shape of `amd-smi metric -g 0 -c --json`: one entry per XCD shader
+    # clock (gfx_0 .. gfx_7) beside other clock domains
+    clocks = {"gfx_%d" % i: {"clk": {"value": v, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"},
+                              "max_clk": {"value": 2400, "unit": "MHz"}} for i, v in enumerate(mhz)}
+    clocks["mem_0"] = {"clk": {"value": 2000, "unit": "MHz"}}
+    return json.dumps({"gpu_data": [{"gpu": 0, "clock": clocks}]})
+
+
+def test_clock_sampler_averages_the_xcd_clocks(monkeypatch):
+    import subprocess
+    outs = iter([_smi_json([1900 + 10 * i for i in range(8)]), _smi_json([2000] * 8)] * 50)
+
+    class R:
+        def __init__(self, out):
+            self.stdout = out
+
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: R(next(outs)))
+    s = bench.ClockSampler(interval=0.0)
+    first, second = s._one(), s._one()
+    assert first == 1935.0 and second == 2000.0      # mean over gfx_0..7, mem_0 ignored
+    s.samples = [first, second]
+    rep = s.summary()
+    assert rep["samples"] == 2 and rep["mean_mhz"] == 1967.5
+    assert rep["min_mhz"] == 1935.0 and rep["max_mhz"] == 2000.0
+
+
+def test_clock_sampler_reports_a_missing_tool(monkeypatch):
+    import subprocess
+
+    def missing(*a, **k):
+        raise FileNotFoundError("amd-smi")
+
+    monkeypatch.setattr(subprocess, "run", missing)
+    s = bench.ClockSampler(interval=0.0).start()
+    rep = s.stop()
+    assert "error" in rep and "FileNotFoundError" in rep["error"]
