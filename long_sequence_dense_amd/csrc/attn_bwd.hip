@@ -299,14 +299,33 @@ __global__ __launch_bounds__(DKDV_THREADS, 1) void bwd_dkdv_kernel(DkdvParams p)
     if (more) stage((t + 1) * TR, buf ^ 1);
     const uint16_t* qt = sm.q[buf];
     const uint16_t* dt = sm.dout[buf];
-    // S = Q K^T and dP = dO V^T for this wave's keys: rows = queries.
-    f32x16 s = (f32x16)0.0f, dp = (f32x16)0.0f;
+    // S = Q K^T and dP = dO V^T for this wave's keys: rows = queries.  16
+    // fenced slots, S first, each reading the operands of the MFMA three
+    // slots later (left to the compiler, each dP MFMA waited on its own
+    // reads).  Each product accumulates over the channel chunks in order.
+    f32x16 s, dp;
+    {
+      constexpr int RA = 3;
+      bf16x8 ra[16], rv[8];
+      auto rd = [&](int i) {
+        if (i < 8) {
+          ra[i] = row_operand(qt, ln, i);
+        } else {
+          ra[i] = row_operand(dt, ln, i - 8);
+          rv[i - 8] = __builtin_bit_cast(bf16x8, *(const u16x8*)(sm.v + v_lane + 16 * (i - 8)));
+        }
+      };
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s = mfma(row_operand(qt, ln, kk), kreg[kk], s);
+      for (int i = 0; i < RA; ++i) rd(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      dp = mfma(row_operand(dt, ln, kk), __builtin_bit_cast(bf16x8, *(const u16x8*)(sm.v + v_lane + 16 * kk)),
-                dp);
+      for (int i = 0; i < 16; ++i) {
+        if (i + RA < 16) rd(i + RA);
+        if (i < 8) s = mfma(ra[i], kreg[i], i == 0 ? (f32x16)0.0f : s);
+        else dp = mfma(ra[i], rv[i - 8], i == 8 ? (f32x16)0.0f : dp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     // P = exp2(S c - m) / l and dS = P (dP - D); accumulator element i is
     // query row 8 * (i / 4) + 4 * hf + i % 4 of the tile.  Then dV^T += dO^T P
     // and dK^T += Q^T dS (16-query chunks cc, channel blocks db) as 16 fenced
@@ -484,11 +503,24 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
     // S^T = K Q^T and dP^T = V dO^T: rows = keys of the tile, columns = this
     // wave's queries; accumulator element i is key 8 * (i / 4) + 4 * hf + i % 4
     // of the tile.  Keys past L are zero rows.
-    f32x16 s = (f32x16)0.0f, dp = (f32x16)0.0f;
+    // 16 fenced slots, S^T first, operands read three slots ahead; each
+    // product accumulates over the channel chunks in order.
+    f32x16 s, dp;
+    {
+      constexpr int RA = 3;
+      bf16x8 ra[16];
+      auto rd = [&](int i) { ra[i] = i < 8 ? row_operand(kt, ln, i) : row_operand(vt, ln, i - 8); };
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s = mfma(row_operand(kt, ln, kk), qreg[kk], s);
+      for (int i = 0; i < RA; ++i) rd(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) dp = mfma(row_operand(vt, ln, kk), doreg[kk], dp);
+      for (int i = 0; i < 16; ++i) {
+        if (i + RA < 16) rd(i + RA);
+        if (i < 8) s = mfma(ra[i], qreg[i], i == 0 ? (f32x16)0.0f : s);
+        else dp = mfma(ra[i], doreg[i - 8], i == 8 ? (f32x16)0.0f : dp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     f32x8 df[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
