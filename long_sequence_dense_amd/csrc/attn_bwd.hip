@@ -504,10 +504,16 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
     // wave's queries; accumulator element i is key 8 * (i / 4) + 4 * hf + i % 4
     // of the tile.  Keys past L are zero rows.
     // 16 fenced slots, S^T first, operands read three slots ahead; each
-    // product accumulates over the channel chunks in order.
+    // product accumulates over the channel chunks in order.  P = exp2(S c -
+    // m) / l is taken during the dP^T slots (S^T is complete by then), and
+    // the first transpose reads of dQ^T += K^T dS^T in the last two.
     f32x16 s, dp;
+    float pv[16];
+    bf16x8 ta[8];
+    auto trd = [&](int j) { ta[j] = tr_operand(kt, ln, j >> 2, j & 3); };
     {
       constexpr int RA = 3;
+      constexpr int kExp[7] = {0, 3, 6, 9, 12, 14, 16};   // P values taken in slots 10..15
       bf16x8 ra[16];
       auto rd = [&](int i) { ra[i] = i < 8 ? row_operand(kt, ln, i) : row_operand(vt, ln, i - 8); };
 #pragma unroll
@@ -516,25 +522,37 @@ __global__ __launch_bounds__(DQ_THREADS, 1) void bwd_dq_kernel(DqParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (i + RA < 16) rd(i + RA);
+        if (i >= 14) trd(i - 14);
         if (i < 8) s = mfma(ra[i], qreg[i], i == 0 ? (f32x16)0.0f : s);
         else dp = mfma(ra[i], doreg[i - 8], i == 8 ? (f32x16)0.0f : dp);
+        if (i >= 10) {
+#pragma unroll
+          for (int e = kExp[i - 10]; e < kExp[i - 9]; ++e)
+            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], p.c, -m)) * invl;
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // dS = P (dP - D); dQ^T += K^T dS^T (keys past L: zero K rows add
+    // nothing) as 8 fenced slots: the chunk-0 MFMAs while dS of chunk 1 is
+    // formed, transpose reads two MFMAs ahead.
     f32x8 df[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -m)) * invl;
-      df[i >> 3][i & 7] = pv * (dp[i] - dsum);
-    }
     bf16x8 dsb[2];
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) dsb[cc] = __builtin_convertvector(df[cc], bf16x8);
-    // dQ^T += K^T dS^T (keys past L: zero K rows add nothing)
+    for (int e = 0; e < 8; ++e) df[0][e] = pv[e] * (dp[e] - dsum);
+    dsb[0] = __builtin_convertvector(df[0], bf16x8);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) dqacc[db] = mfma(tr_operand(kt, ln, cc, db), dsb[cc], dqacc[db]);
+    for (int j = 0; j < 8; ++j) {
+      if (j + 2 < 8) trd(j + 2);
+      dqacc[j & 3] = mfma(ta[j], dsb[j >> 2], dqacc[j & 3]);
+      if (j < 4) {
+        df[1][2 * j] = pv[8 + 2 * j] * (dp[8 + 2 * j] - dsum);
+        df[1][2 * j + 1] = pv[9 + 2 * j] * (dp[9 + 2 * j] - dsum);
+        if (j == 3) dsb[1] = __builtin_convertvector(df[1], bf16x8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     if (more) {
       store_rows(sm.k[buf ^ 1], tid, sk);
