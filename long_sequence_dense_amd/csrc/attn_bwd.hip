@@ -42,6 +42,10 @@
 //               per workgroup; Q and dO of its rows in registers, 32-key tiles
 //               of K and V through LDS; S^T = K Q^T, dP^T = V dO^T, dS^T on
 //               the VALU, dQ^T += K^T dS^T.
+// In both gradient kernels the products of a tile run as fenced MFMA slots
+// (sched_barrier) with their LDS operands read two or three MFMAs ahead and
+// the exponentials and dS arithmetic placed between MFMAs that do not need
+// them, so that no MFMA waits on a read issued just before it.
 // Seven of the 2 H L^2 d products per call (S and dP twice, dV, dK, dQ).
 // P and dS are rounded to BF16 for their MFMAs; all sums are fp32.  Rows past
 // L are zero-filled by the buffer loads: their keys add nothing to dQ (zero K
