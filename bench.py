@@ -487,7 +487,7 @@ def main():
                                 "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
         paths["attn_fwd_fp4qk"] = {"ms": round(t_fp4, 3), "TFLOP/s": round(a4, 1),
                                    "frac_of_peak": round(a4 / PEAK_BF16_TFLOPS, 4),
-                                   "mfma_precision": "bf16 (exact dequantization of NVFP4 Q/K)"}
+                                   "mfma_precision": "fp16 scores (exact dequantization of NVFP4 Q/K), bf16 P.V"}
     if args.only != "bf16":
         # Extra path, outside the step's value: the fused-Q form of the FP4
         # path (K-only prep, then attention that quantizes Q in its prologue)

@@ -208,7 +208,8 @@ int qk_prep_fp4_noalloc(const uint16_t* q, const uint16_t* k,
  *   v   : [H, L, d] BF16 bits.   o : [H, L, d] BF16 bits, written.
  *   lse : optional [H, L] float32 (NULL to skip).
  * Scores are softmax_scale * (Qhat . Khat) where Qhat, Khat are the exact
- * dequantized values (E2M1 times E4M3: at most 6 significant bits, so exact in
+ * dequantized values (E2M1 times E4M3: at most 6 significant bits in
+ * [2^-10, 2688], so exact in FP16, in which the score products run, and in
  * BF16); the rest is as in attn_fwd_bf16.  Because the smoothing and the
  * orthonormal rotation change no score before quantization, O approximates
  * attn_fwd_bf16 on the original Q, K.

@@ -39,9 +39,13 @@
 //   * Workgroups are renumbered so that each XCD (own L2) processes a
 //     contiguous range of query tiles of one head, which then stream the same
 //     K/V tiles at about the same time.
-//   * The FP4-QK variant dequantizes each K tile (E2M1 x E4M3, exact in BF16)
-//     into the same LDS layout, and its Q rows once, then runs the same
-//     pipeline on BF16 MFMA.  Its fused-Q form takes Q in BF16 and applies
+//   * The FP4-QK variant dequantizes each K tile into the same LDS layout,
+//     and its Q rows once, to FP16 (E2M1 x E4M3 products have at most 6
+//     significant bits in [2^-10, 2688]: exact; the hardware FP4-to-FP16
+//     pair conversion and one packed FP16 multiply per pair), then runs the
+//     same pipeline with the score MFMAs in their FP16 form (same rate, same
+//     exact products and fp32 sums as BF16 operands would give; P.V stays
+//     BF16).  Its fused-Q form takes Q in BF16 and applies
 //     the prep's rotation and quantizer to each wave's rows in the prologue
 //     (the same fp32 operations in the same order, so the same codes), then
 //     dequantizes them in registers: Q's codes never go through memory.
@@ -96,11 +100,20 @@ struct Smem {
   uint16_t v[2][BC * VS];
 };
 
-// 16 NVFP4 values (8 code bytes + 1 scale byte) to 16 BF16 bit patterns.
+// 16 NVFP4 values (8 code bytes + 1 scale byte) to 16 FP16 bit patterns.
 __device__ __forceinline__ void dequant16(uint64_t codes, uint32_t scale_byte, u16x8& lo, u16x8& hi) {
-  const float s = e4m3_to_f32(scale_byte);
-  lo = dequant8((uint32_t)codes, s);
-  hi = dequant8((uint32_t)(codes >> 32), s);
+  const _Float16 s = e4m3_to_f16(scale_byte);
+  lo = dequant8_h((uint32_t)codes, s);
+  hi = dequant8_h((uint32_t)(codes >> 32), s);
+}
+
+// Score MFMA: BF16 operands, or (FP4-QK) the exactly dequantized FP16 ones.
+template <bool F16>
+__device__ __forceinline__ f32x16 score_mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h16x8, a), __builtin_bit_cast(h16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
@@ -185,7 +198,7 @@ __device__ __forceinline__ bf16x8 k_operand(const uint16_t* kl, int i) {   // i 
 }
 
 // The first KPRE operands come from registers read earlier (kpre).
-template <int NPRE>
+template <int NPRE, bool F16 = false>
 __device__ __forceinline__ void qk_tile(const uint16_t* kl, const bf16x8 (&kpre)[KPRE], const bf16x8 (&qreg)[8],
                                         f32x16 (&s)[2]) {
 #pragma unroll
@@ -195,7 +208,7 @@ __device__ __forceinline__ void qk_tile(const uint16_t* kl, const bf16x8 (&kpre)
     for (int kk = 0; kk < 8; ++kk) {
       const int i = 8 * b + kk;
       const bf16x8 a = i < NPRE ? kpre[i < KPRE ? i : 0] : k_operand(kl, i);
-      s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s[b], 0, 0, 0);
+      s[b] = score_mfma<F16>(a, qreg[kk], s[b]);
     }
   }
 }
@@ -339,33 +352,32 @@ __device__ __forceinline__ void qk_stage_tile(const uint16_t* kl, const bf16x8 (
   for (int i = 0; i < KPRE; ++i) ka[i] = kpre[i];
   s[0] = (f32x16)0.0f;
   s[1] = (f32x16)0.0f;
-  float f[16];
-  float sc = 0.0f;
-  if constexpr (FP4 && STORE) sc = e4m3_to_f32(kr.scale[0] & 0xFF);
+  u32x4 hw[2];
+  h16x2 s2 = {(_Float16)0.0f, (_Float16)0.0f};
+  if constexpr (FP4 && STORE) {
+    const _Float16 sc = e4m3_to_f16(kr.scale[0] & 0xFF);
+    s2 = h16x2{sc, sc};
+  }
   const int key = tid >> 3, blk = tid & 7;       // FP4 staging: this thread's block
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (j + KPRE < 16) ka[j + KPRE] = k_operand(kl, j + KPRE);
-    s[j >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j], qreg[j & 7], s[j >> 3], 0, 0, 0);
+    s[j >> 3] = score_mfma<true>(ka[j], qreg[j & 7], s[j >> 3]);
     if constexpr (STORE) {
       if constexpr (FP4) {
         if (j < 8) {
           const uint32_t w = kr.codes[0][j >> 2];
-          float lo = 0.0f, hi = 0.0f;
+          uint32_t v = 0;
           switch (j & 3) {                       // the byte select must be a constant
-            case 0: { const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); lo = a[0]; hi = a[1]; break; }
-            case 1: { const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); lo = a[0]; hi = a[1]; break; }
-            case 2: { const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); lo = a[0]; hi = a[1]; break; }
-            default: { const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); lo = a[0]; hi = a[1]; break; }
+            case 0: v = fp4_pair_h<0>(w, s2); break;
+            case 1: v = fp4_pair_h<1>(w, s2); break;
+            case 2: v = fp4_pair_h<2>(w, s2); break;
+            default: v = fp4_pair_h<3>(w, s2); break;
           }
-          f[2 * j] = lo * sc;
-          f[2 * j + 1] = hi * sc;
+          hw[j >> 2][j & 3] = v;
         } else if (j < 10) {
           const int h = j - 8;
-          u16x8 r;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) r[e] = (uint16_t)(__float_as_uint(f[8 * h + e]) >> 16);
-          *(u16x8*)(kb + key * KS + 16 * blk + 8 * h) = r;
+          *(u32x4*)(kb + key * KS + 16 * blk + 8 * h) = hw[h];
         }
       }
     }
@@ -518,7 +530,7 @@ __device__ __forceinline__ void quant_dequant_q(const uint16_t* qp, bool valid, 
     float t[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) t[j] = div_scale(x[kk][j], s, rinv);
-    qreg[kk] = __builtin_bit_cast(bf16x8, dequant8(e2m1_pack8(t), s));
+    qreg[kk] = __builtin_bit_cast(bf16x8, dequant8_h(e2m1_pack8(t), e4m3_to_f16(sc)));
   }
 }
 
@@ -581,8 +593,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
     for (int kk = 0; kk < 8; ++kk) {
       // channels 16kk + 8hf .. +7 live in code bytes 8kk + 4hf .. +3
       const uint32_t c4 = qvalid ? *(const uint32_t*)(cp + 8 * kk + 4 * hf) : 0u;
-      const float s = e4m3_to_f32(qvalid ? sp[kk] : 0u);
-      st.qreg[kk] = __builtin_bit_cast(bf16x8, dequant8(c4, s));
+      const _Float16 s = e4m3_to_f16(qvalid ? sp[kk] : 0u);
+      st.qreg[kk] = __builtin_bit_cast(bf16x8, dequant8_h(c4, s));
     }
   }
 
@@ -599,7 +611,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(AttnParams p) {
   __syncthreads();
   {
     bf16x8 none[KPRE];
-    qk_tile<0>(sm.k[0] + cx.k_lane, none, st.qreg, st.s);
+    qk_tile<0, FP4>(sm.k[0] + cx.k_lane, none, st.qreg, st.s);
   }
   __syncthreads();                      // K(0)'s buffer is refilled with K(2) in the first iteration
 

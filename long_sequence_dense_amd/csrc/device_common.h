@@ -42,6 +42,37 @@ __device__ __forceinline__ void fp4_pair(uint32_t w, float s, float* f) {
   f[2 * J + 1] = a[1] * s;
 }
 
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+
+// E4M3 code to FP16, exactly: the bits (code & 0x7F) << 7 read as FP16 carry
+// the exponent and mantissa fields (biases 15 vs 7; a zero exponent lands on
+// an FP16 subnormal of the same form), times 2^8; bit 7 is the sign.
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t code) {
+  const _Float16 mag = __builtin_bit_cast(_Float16, (uint16_t)((code & 0x7Fu) << 7)) * (_Float16)256.0f;
+  return (code & 0x80u) ? -mag : mag;
+}
+
+// Two FP4 codes (byte J of w) decoded exactly by the hardware to FP16 (unit
+// scale), times the FP16 block scale: one packed multiply, exact.
+template <int J>
+__device__ __forceinline__ uint32_t fp4_pair_h(uint32_t w, h16x2 s2) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, J) * s2);
+}
+
+// 8 codes (one dword, low nibble first) times the FP16 scale s -> 8 FP16 bit
+// patterns.  E2M1 x E4M3 products have at most 6 significant bits and lie in
+// [2^-10, 2688] when nonzero: exact FP16 normals.
+__device__ __forceinline__ u16x8 dequant8_h(uint32_t w, _Float16 s) {
+  const h16x2 s2 = {s, s};
+  u32x4 r;
+  r[0] = fp4_pair_h<0>(w, s2);
+  r[1] = fp4_pair_h<1>(w, s2);
+  r[2] = fp4_pair_h<2>(w, s2);
+  r[3] = fp4_pair_h<3>(w, s2);
+  return __builtin_bit_cast(u16x8, r);
+}
+
 // 8 codes (one dword, low nibble first) times scale s -> 8 BF16 bit patterns.
 // Every product E2M1 x E4M3 has at most 6 significant bits and lies in
 // [2^-10, 2688], so the float32 product is exact and truncating it to BF16 is
