@@ -355,6 +355,31 @@ def test_fp4qk_full_size_sampled(torch):
     assert not torch.isnan(o).any().item()
 
 
+@pytest.mark.parametrize("H,L", [(2, 1024), (2, 65), (1, 200), (3, 4000)])
+def test_fp4qk_equals_bf16_on_dequantized(torch, H, L):
+    """The FP4-QK attention is the BF16 attention on the exactly dequantized
+    Q-hat, K-hat: every E2M1 x E4M3 value is exact in BF16 (and in the FP16 the
+    FP4 kernel multiplies in), the products are exact, and the sums run in the
+    same order, so O and the LSE agree bit for bit."""
+    from long_sequence_dense_amd import binding
+    from oracle.nvfp4 import dequant_nvfp4
+    d = inputs.make_inputs("fp4", H=H, L=L)
+    say("case fp4qk == bf16 on dequantized H=%d L=%d" % (H, L))
+    o4, l4 = run_fp4(torch, d)
+    prep = run_prep(torch, d)
+    hat = {}
+    for n in ("q", "k"):
+        vals = dequant_nvfp4(prep[n + "_codes"].cpu().numpy(), prep[n + "_scales"].cpu().numpy())
+        bits = inputs.f32_to_bf16_bits(vals.astype(np.float32))
+        assert np.array_equal(f64(bits), vals), n          # exact in BF16
+        hat[n] = bits
+    ob, lb = run_bf16(torch, {"q": hat["q"], "k": hat["k"], "v": d["v"], "scale": d["scale"]})
+    same_o = torch.equal(o4.view(torch.int16), ob.view(torch.int16))
+    same_l = torch.equal(l4, lb)
+    say("  O bit-identical %s, LSE bit-identical %s" % (same_o, same_l))
+    assert same_o and same_l
+
+
 def test_offsets_beyond_2gib(torch):
     """80 heads of the 15-second FP4 workload: every BF16 tensor is 2.23 GB,
     so the last heads start past 2^31 bytes.  BF16 attention, the prep (every
