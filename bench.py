@@ -12,7 +12,7 @@ After the timed steps (outside them) the line also carries the extra paths
 CPU oracle baseline and the standalone matrix-core probe's sustained BF16 MFMA
 rate for random and all-zero operands (the attainable ceiling under this GPU's
 power limit, against which roofline.achieved is also read).  The shader
-clock is sampled with amd-smi while the timed steps run.  The step's prep
+clock and socket power are sampled with amd-smi while the timed steps run.  The step's prep
 follows the BF16 launch, which streams 2.2 GB of other tensors through the
 256 MB memory-side cache, so it starts cold; the separately timed
 memory-bound calls (K-only prep, NVFP4 quantizer) are each preceded by a
@@ -217,13 +217,14 @@ class MallFlush:
 
 
 class ClockSampler:
-    """Samples the GPU's shader clock with `amd-smi metric -c` (the mean of
-    the eight XCD clocks per sample) from a background thread while the timed
-    steps run."""
+    """Samples the GPU's shader clock and socket power with `amd-smi metric -c
+    -p` (the mean of the eight XCD clocks per sample) from a background thread
+    while the timed steps run."""
 
-    def __init__(self, interval=0.25):
+    def __init__(self, interval=0.25, window="the timed steps (both attention launches and the prep)"):
         import threading
         self.interval = interval
+        self.window = window
         self.samples = []
         self.error = None
         self.stop_event = threading.Event()
@@ -231,12 +232,15 @@ class ClockSampler:
 
     def _one(self):
         import subprocess
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], stdout=subprocess.PIPE,
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], stdout=subprocess.PIPE,
                            stderr=subprocess.PIPE, text=True, timeout=20)
-        d = json.loads(r.stdout)
-        clocks = d["gpu_data"][0]["clock"]
-        vals = [float(v["clk"]["value"]) for k, v in clocks.items() if k.startswith("gfx_")]
-        return sum(vals) / len(vals)
+        d = json.loads(r.stdout)["gpu_data"][0]
+        vals = [float(v["clk"]["value"]) for k, v in d["clock"].items() if k.startswith("gfx_")]
+        try:
+            watts = float(d["power"]["socket_power"]["value"])
+        except (KeyError, TypeError, ValueError):
+            watts = None
+        return sum(vals) / len(vals), watts
 
     def _run(self):
         while not self.stop_event.is_set():
@@ -260,11 +264,15 @@ class ClockSampler:
     def summary(self):
         if not self.samples:
             return {"error": self.error or "no sample"}
-        xs = self.samples
-        return {"source": "amd-smi metric -c, mean of the 8 XCD shader clocks per sample",
-                "window": "the timed steps (both attention launches and the prep)",
-                "samples": len(xs), "mean_mhz": round(sum(xs) / len(xs), 1),
-                "min_mhz": round(min(xs), 1), "max_mhz": round(max(xs), 1)}
+        xs = [c for c, _ in self.samples]
+        ws = [w for _, w in self.samples if w is not None]
+        rep = {"source": "amd-smi metric -c -p: mean of the 8 XCD shader clocks, socket power",
+               "window": self.window,
+               "samples": len(xs), "mean_mhz": round(sum(xs) / len(xs), 1),
+               "min_mhz": round(min(xs), 1), "max_mhz": round(max(xs), 1)}
+        if ws:
+            rep.update({"mean_socket_w": round(sum(ws) / len(ws), 1), "max_socket_w": round(max(ws), 1)})
+        return rep
 
 
 def linear_path(torch, binding, stream, dev):
@@ -456,7 +464,8 @@ def main():
         step(False)
     torch.cuda.synchronize()
     log("timing %d steps ..." % args.steps)
-    sampler = ClockSampler().start()
+    sampler = ClockSampler(window="the timed steps (attn_fwd_bf16 only)" if args.only == "bf16" else
+                           "the timed steps (both attention launches and the prep)").start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(True)

@@ -63,7 +63,8 @@ def _smi_json(mhz):
     clocks = {"gfx_%d" % i: {"clk": {"value": v, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"},
                               "max_clk": {"value": 2400, "unit": "MHz"}} for i, v in enumerate(mhz)}
     clocks["mem_0"] = {"clk": {"value": 2000, "unit": "MHz"}}
-    return json.dumps({"gpu_data": [{"gpu": 0, "clock": clocks}]})
+    power = {"socket_power": {"value": 1400, "unit": "W"}, "gfx_voltage": "N/A"}
+    return json.dumps({"gpu_data": [{"gpu": 0, "clock": clocks, "power": power}]})
 
 
 def test_clock_sampler_averages_the_xcd_clocks(monkeypatch):
@@ -77,11 +78,12 @@ def test_clock_sampler_averages_the_xcd_clocks(monkeypatch):
     monkeypatch.setattr(subprocess, "run", lambda *a, **k: R(next(outs)))
     s = bench.ClockSampler(interval=0.0)
     first, second = s._one(), s._one()
-    assert first == 1935.0 and second == 2000.0      # mean over gfx_0..7, mem_0 ignored
+    assert first == (1935.0, 1400.0) and second == (2000.0, 1400.0)   # mean over gfx_0..7, mem_0 ignored
     s.samples = [first, second]
     rep = s.summary()
     assert rep["samples"] == 2 and rep["mean_mhz"] == 1967.5
     assert rep["min_mhz"] == 1935.0 and rep["max_mhz"] == 2000.0
+    assert rep["mean_socket_w"] == 1400.0 and rep["max_socket_w"] == 1400.0
 
 
 def test_clock_sampler_reports_a_missing_tool(monkeypatch):
