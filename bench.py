@@ -266,12 +266,16 @@ class ClockSampler:
             return {"error": self.error or "no sample"}
         xs = [c for c, _ in self.samples]
         ws = [w for _, w in self.samples if w is not None]
+        def median(v):
+            v = sorted(v)
+            return 0.5 * (v[(len(v) - 1) // 2] + v[len(v) // 2])
         rep = {"source": "amd-smi metric -c -p: mean of the 8 XCD shader clocks, socket power",
                "window": self.window,
-               "samples": len(xs), "mean_mhz": round(sum(xs) / len(xs), 1),
+               "samples": len(xs), "mean_mhz": round(sum(xs) / len(xs), 1), "median_mhz": round(median(xs), 1),
                "min_mhz": round(min(xs), 1), "max_mhz": round(max(xs), 1)}
         if ws:
-            rep.update({"mean_socket_w": round(sum(ws) / len(ws), 1), "max_socket_w": round(max(ws), 1)})
+            rep.update({"mean_socket_w": round(sum(ws) / len(ws), 1), "median_socket_w": round(median(ws), 1),
+                        "max_socket_w": round(max(ws), 1)})
         return rep
 
 
@@ -342,6 +346,51 @@ def bw_ceiling(torch, H, L, d):
     print(json.dumps({"bw_ceiling": res, "tensor": "[%d, %d, %d] bf16" % (H, L, d)}), flush=True)
 
 
+def operand_energy(torch, binding, stream, H, L, d, reps=20):
+    """The shipped attn_fwd_bf16 on the same shape with different operand
+    data: the 15-second inputs as generated, the same with V = 0 and with
+    K = V = 0, and flat N(0,1) Q, K, V (no outlier channels).  Every case runs
+    the same instructions; the shader clock and socket power are sampled
+    during ``reps`` timed calls (after five untimed calls that bring the
+    clock to its level under this load), so that cycles per launch (ms x
+    median clock) and energy per launch (ms x median power) can be compared.
+    Prints one JSON line."""
+    cfg, x = gen_inputs(torch, "clip15s")
+    o = torch.empty_like(x["q"])
+    fl = attn_flop(H, L, d)
+    gen = torch.Generator(device=x["q"].device)
+    gen.manual_seed(11)
+
+    def flat():
+        return torch.randn((H, L, d), dtype=torch.float32, device=x["q"].device, generator=gen).to(torch.bfloat16)
+
+    zeros = torch.zeros_like(x["v"])
+    cases = [("15-second inputs as generated", lambda: (x["q"], x["k"], x["v"])),
+             ("15-second inputs, V = 0", lambda: (x["q"], x["k"], zeros)),
+             ("15-second inputs, K = V = 0", lambda: (x["q"], zeros, zeros)),
+             ("flat N(0,1) Q, K, V", lambda: (flat(), flat(), flat()))]
+    rows = []
+    for name, make in cases:
+        q, k, v = make()
+        log("operand energy: %s ..." % name)
+        for _ in range(5):
+            binding.attn_fwd_bf16(q, k, v, o, None, cfg.scale, stream)
+        torch.cuda.synchronize()
+        sampler = ClockSampler(window="attn_fwd_bf16, " + name).start()
+        t = time_calls(torch, stream, lambda: binding.attn_fwd_bf16(q, k, v, o, None, cfg.scale, stream), n=reps)
+        clk = sampler.stop()
+        row = {"inputs": name, "ms": round(t, 3), "TFLOP/s": round(fl / (t * 1e-3) / 1e12, 1), "clock": clk}
+        if "median_mhz" in clk:
+            row["mcycles_per_launch"] = round(t * clk["median_mhz"] / 1e3, 1)
+        if "median_socket_w" in clk:
+            row["socket_joules_per_launch"] = round(t * clk["median_socket_w"] / 1e3, 1)
+            row["socket_pj_per_flop"] = round(t * 1e-3 * clk["median_socket_w"] / fl * 1e12, 3)
+        rows.append(row)
+        del q, k, v
+    print(json.dumps({"operand_energy": rows, "kernel": "attn_fwd_bf16",
+                      "shape": "H=%d, L=%d, d=%d" % (H, L, d), "calls_per_case": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +412,9 @@ def main():
     ap.add_argument("--bw-ceiling", action="store_true",
                     help="time plain read-only, copy and write-only passes over tensors of the prep's sizes "
                          "(the bandwidth ceiling its kernels are compared with); prints one JSON line")
+    ap.add_argument("--operand-energy", action="store_true",
+                    help="time attn_fwd_bf16 on the benchmark shape with its inputs as generated, with V = 0, "
+                         "with K = V = 0 and on flat N(0,1) inputs, sampling clock and power; prints one JSON line")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for hardware-counter runs: one %d-byte torch copy (counter calibration), "
                          "then one launch of each kernel on the benchmark workload; no timing" % COPY_PROBE_BYTES)
@@ -384,6 +436,9 @@ def main():
     H, L, d = 40, 109000, 128
     if args.bw_ceiling:
         bw_ceiling(torch, H, L, d)
+        return
+    if args.operand_energy:
+        operand_energy(torch, binding, torch.cuda.current_stream(), H, L, d)
         return
 
     log("generating inputs (seeded, synthetic) ...")

@@ -84,6 +84,10 @@ def test_clock_sampler_averages_the_xcd_clocks(monkeypatch):
     assert rep["samples"] == 2 and rep["mean_mhz"] == 1967.5
     assert rep["min_mhz"] == 1935.0 and rep["max_mhz"] == 2000.0
     assert rep["mean_socket_w"] == 1400.0 and rep["max_socket_w"] == 1400.0
+    assert rep["median_mhz"] == 1967.5 and rep["median_socket_w"] == 1400.0
+    s.samples = [(1200.0, 900.0), (2000.0, 1300.0), (2010.0, 1310.0)]    # one sample before the clock settled
+    rep = s.summary()
+    assert rep["median_mhz"] == 2000.0 and rep["median_socket_w"] == 1300.0
 
 
 def test_clock_sampler_reports_a_missing_tool(monkeypatch):
