@@ -84,8 +84,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) { return __builtin_
 
 // Memory -> LDS without registers: buffer_load_dword with the LDS flag writes
 // lane j's dword to M0 + 4 j (one 256-byte row per wave instruction).  Byte
-// offsets go in the per-lane offset so the range check sees them: rows past
-// the end are written as zeros.  Inline assembly so that the compiler does
+// offsets go in the per-lane offset; the resource's range check applies to
+// the per-lane plus the scalar offset, so rows past the end are written as
+// zeros.  Inline assembly so that the compiler does
 // not wait for these loads before reading the other LDS buffer; the caller
 // waits (vmcnt 0) before the barrier that publishes the data.  M0 is written
 // by SALU and read by the load one instruction later (s_nop: the M0 read

@@ -118,6 +118,11 @@ def head_tensor(cfg, which, head):
     tid = {"q": TID_Q, "k": TID_K, "v": TID_V, "do": TID_DOUT}[which]
     dist = {"q": cfg.q_dist, "k": cfg.k_dist, "v": cfg.v_dist, "do": "normal"}[which]
     x = _draw(dist, _rng(cfg.seed, tid, head), cfg.L)
+    return _finish(cfg, which, head, x)
+
+
+def _finish(cfg, which, head, x):
+    """Row-wise scaling and offset of float32 draws x [n, d], then BF16 bits."""
     if which == "q" and cfg.q_prescale:
         x *= np.float32(INV_SQRT_D)
     if which in ("q", "k") and cfg.outliers:
@@ -127,6 +132,31 @@ def head_tensor(cfg, which, head):
         off = _rng(cfg.seed, TID_OFFSET, head).normal(0.0, math.sqrt(2.0), D)
         x = (x.astype(np.float64) + off[None, :]).astype(np.float32)
     return f32_to_bf16_bits(x)
+
+
+# A single long head (millions of tokens) is drawn in chunks of LONG_CHUNK
+# rows, chunk c from Generator(PCG64(SeedSequence([seed, tensor_id, head,
+# LONG_TAG + c]))), in a thread pool; the distribution, scaling, offset and
+# rounding are those of head_tensor (a different stream of the same law).
+LONG_CHUNK = 1 << 18
+LONG_TAG = 1 << 20
+
+
+def long_head_tensor(cfg, which, head=0):
+    """One head of Q, K, V or dO as BF16 bits [L, d], drawn chunk-wise."""
+    tid = {"q": TID_Q, "k": TID_K, "v": TID_V, "do": TID_DOUT}[which]
+    dist = {"q": cfg.q_dist, "k": cfg.k_dist, "v": cfg.v_dist, "do": "normal"}[which]
+    out = np.empty((cfg.L, D), dtype=np.uint16)
+
+    def fill(c):
+        r0 = c * LONG_CHUNK
+        n = min(LONG_CHUNK, cfg.L - r0)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, tid, head, LONG_TAG + c])))
+        out[r0:r0 + n] = _finish(cfg, which, head, _draw(dist, rng, n))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range((cfg.L + LONG_CHUNK - 1) // LONG_CHUNK)))
+    return out
 
 
 def _threads():

@@ -380,6 +380,30 @@ def test_fp4qk_equals_bf16_on_dequantized(torch, H, L):
     assert same_o and same_l
 
 
+def test_bf16_max_head_length(torch):
+    """The longest head the library accepts, L = 2^23 - 1 = 8,388,607 tokens
+    (one head of the 15-second input structure, drawn chunk-wise; 2 GiB -
+    256 B per BF16 tensor): the last K/V tile starts 16 KiB before 2^31 bytes
+    into the head and is ragged (63 of its 64 keys).  BF16 attention on
+    sampled query rows (the first and last rows of every tile size at both
+    ends included) against the fp64 oracle over all keys; no output left
+    unwritten."""
+    from oracle.attention import attention_fp64
+    L = (1 << 23) - 1
+    c = inputs.CONFIGS["clip15s"].with_shape(H=1, L=L)
+    say("case max head length: clip15s structure H=1 L=%d (generate)" % L)
+    d = {w: inputs.long_head_tensor(c, w)[None] for w in ("q", "k", "v")}
+    d["scale"] = c.scale
+    say("  bf16 attention")
+    o, l = run_bf16(torch, d)
+    assert not torch.isnan(o).any().item()
+    assert not torch.isnan(l).any().item()
+    rows = inputs.sample_rows(L, 24)
+    say("  oracle on %d rows over %d keys" % (len(rows), L))
+    oref, lref = attention_fp64(f64(d["q"][:, rows]), f64(d["k"]), f64(d["v"]), d["scale"])
+    check_attention("bf16 L=2^23-1 sampled", o, l, oref, lref, rows=rows)
+
+
 def test_offsets_beyond_2gib(torch):
     """80 heads of the 15-second FP4 workload: every BF16 tensor is 2.23 GB,
     so the last heads start past 2^31 bytes.  BF16 attention, the prep (every

@@ -93,3 +93,28 @@ def test_linear_operands_rows_regenerate():
     assert 15 < np.std(xf[:, ch]) < 25 and 0.9 < np.std(np.delete(xf, ch, axis=1)) < 1.1
     w = inputs.bf16_bits_to_f32(inputs.linear_operand("w", 256, 1024, 4))
     assert abs(np.var(w) * 1024 - 1) < 0.05
+
+
+def test_long_head_chunks():
+    """The chunked generator of one long head: deterministic, each chunk its
+    own stream (regenerated alone here), the ragged last chunk, and the
+    outlier channels of the 15-second structure."""
+    cfg = inputs.CONFIGS["clip15s"].with_shape(H=1, L=2 * inputs.LONG_CHUNK + 1000)
+    a = inputs.long_head_tensor(cfg, "q")
+    assert a.shape == (cfg.L, 128) and a.dtype == np.uint16
+    assert np.array_equal(a, inputs.long_head_tensor(cfg, "q"))
+    ch = inputs.outlier_channels(cfg, 0)
+    for c, n in ((1, inputs.LONG_CHUNK), (2, 1000)):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+            [cfg.seed, inputs.TID_Q, 0, inputs.LONG_TAG + c])))
+        x = rng.standard_normal((n, 128), dtype=np.float32)
+        x[:, ch] *= np.float32(20.0)
+        r0 = c * inputs.LONG_CHUNK
+        assert np.array_equal(a[r0:r0 + n], inputs.f32_to_bf16_bits(x))
+    assert not np.array_equal(a[:1000], a[inputs.LONG_CHUNK:inputs.LONG_CHUNK + 1000])
+    q = inputs.bf16_bits_to_f32(a).astype(np.float64)
+    med = np.median(np.abs(q), axis=0)
+    others = np.setdiff1d(np.arange(128), ch)
+    assert np.all(med[ch] > 10 * np.max(med[others]))
+    v = inputs.bf16_bits_to_f32(inputs.long_head_tensor(cfg, "v")).astype(np.float64)
+    assert abs(np.std(v) - 1.0) < 0.01
