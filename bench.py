@@ -324,26 +324,22 @@ def config_path(torch, binding, stream, name, reps):
             "workload": cfg.desc, "in_value": False}
 
 
-def bw_ceiling(torch, H, L, d):
-    """Plain passes over a [H, L, d] BF16 tensor (one of the prep's inputs,
-    1.116 GB) with torch's own kernels: a read-only reduction (amax), a copy
-    (read + write) and a write-only fill of a code-sized buffer; 2 warm-ups, 5
-    timed calls each, HIP events on the current stream."""
-    stream = torch.cuda.current_stream()
-    x = torch.randn((H, L, d), device="cuda").to(torch.bfloat16)
-    y = torch.empty_like(x)
-    c = torch.empty((H, L, d // 2 + d // 16), dtype=torch.uint8, device="cuda")
-    nx, nc = x.numel() * 2, c.numel()
-    res = {}
-    for name, fn, nbytes in (("read_only_amax", lambda: x.amax(), nx),
-                             ("copy_read_write", lambda: y.copy_(x), 2 * nx),
-                             ("write_only_fill", lambda: c.fill_(7), nc)):
-        for _ in range(2):
-            fn()
-        t = time_calls(torch, stream, fn, n=5)
-        res[name] = {"ms": round(t, 4), "bytes": nbytes, "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1),
-                     "frac_of_peak": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    print(json.dumps({"bw_ceiling": res, "tensor": "[%d, %d, %d] bf16" % (H, L, d)}), flush=True)
+def bw_ceiling():
+    """Run the standalone HBM probe (built in-tree by the library's build
+    step): read-only, copy and write-only passes with 16-byte accesses over a
+    tensor of the prep's input size (1.116 GB) and its code and scale bytes,
+    ordinary and non-temporal loads, the memory-side cache replaced by clean
+    lines before each launch.  None if it is not built."""
+    import subprocess
+    exe = os.path.join(ROOT, "long_sequence_dense_amd", "hbm_ceiling_probe")
+    if not os.path.exists(exe):
+        log("hbm_ceiling_probe not built; skipped")
+        return None
+    log("running the HBM ceiling probe ...")
+    r = subprocess.run([exe], stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+    if r.returncode != 0:
+        raise RuntimeError("hbm_ceiling_probe failed (%d): %s" % (r.returncode, r.stderr.strip()))
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def operand_energy(torch, binding, stream, H, L, d, reps=20):
@@ -399,6 +395,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
                     help="skip the standalone MFMA ceiling probe (random vs zero operands) after the timed steps")
+    ap.add_argument("--no-hbm-ceiling", action="store_true",
+                    help="skip the standalone HBM ceiling probe (read-only, copy, write-only) after the timed steps")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the standalone MFMA ceiling probe and print its JSON line")
     ap.add_argument("--only", choices=["all", "bf16"], default="all",
@@ -410,8 +408,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the extra (not in value) BF16 timings of the 24 x 8192 and 40 x 36,480 workloads")
     ap.add_argument("--bw-ceiling", action="store_true",
-                    help="time plain read-only, copy and write-only passes over tensors of the prep's sizes "
-                         "(the bandwidth ceiling its kernels are compared with); prints one JSON line")
+                    help="only run the standalone HBM probe (read-only, copy and write-only passes over "
+                         "tensors of the prep's sizes: the ceilings its kernels are compared with) and "
+                         "print its JSON line")
     ap.add_argument("--operand-energy", action="store_true",
                     help="time attn_fwd_bf16 on the benchmark shape with its inputs as generated, with V = 0, "
                          "with K = V = 0 and on flat N(0,1) inputs, sampling clock and power; prints one JSON line")
@@ -428,15 +427,15 @@ def main():
     if args.mfma_ceiling:
         print(json.dumps(mfma_ceiling()), flush=True)
         return
+    if args.bw_ceiling:
+        print(json.dumps(bw_ceiling()), flush=True)
+        return
 
     import torch
     from long_sequence_dense_amd import binding
     assert torch.cuda.is_available(), "bench needs a GPU"
     binding.load_library()
     H, L, d = 40, 109000, 128
-    if args.bw_ceiling:
-        bw_ceiling(torch, H, L, d)
-        return
     if args.operand_energy:
         operand_energy(torch, binding, torch.cuda.current_stream(), H, L, d)
         return
@@ -684,6 +683,13 @@ def main():
             rnd = ceil["mfma_ceiling_bf16_TFLOP/s"]["random_operands"]
             ceil["attn_fwd_bf16_frac_of_random_operand_ceiling"] = round(res["roofline"]["achieved"] / rnd, 4)
         res["mfma_ceiling_probe"] = ceil
+    if not args.no_hbm_ceiling:
+        hbm = bw_ceiling()
+        if hbm is not None and "qk_prep_fp4" in res["paths"]:
+            copy = max(v["best"] for k, v in hbm["hbm_ceiling_GB/s"].items() if k.startswith("copy"))
+            hbm["qk_prep_fp4_algorithmic_rate_frac_of_copy_ceiling"] = round(
+                res["paths"]["qk_prep_fp4"]["GB/s"] / copy, 4)
+        res["hbm_ceiling_probe"] = hbm
     print(json.dumps(res), flush=True)
 
 

@@ -2,7 +2,8 @@
 
 Usage: python -m long_sequence_dense_amd.build   (or build() from Python).
 Every call recompiles.  Output: long_sequence_dense_amd/liblsd_attn.so and the
-standalone matrix-core ceiling probe long_sequence_dense_amd/mfma_ceiling_probe.
+standalone ceiling probes long_sequence_dense_amd/mfma_ceiling_probe (matrix
+cores) and long_sequence_dense_amd/hbm_ceiling_probe (HBM streaming rates).
 """
 
 import os
@@ -13,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblsd_attn.so")
-PROBE = os.path.join(HERE, "mfma_ceiling_probe")
+PROBES = ("mfma_ceiling_probe", "hbm_ceiling_probe")
 ARCH = "gfx950"
 
 COMMON = [
@@ -63,10 +64,11 @@ def build(verbose=False):
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
     os.replace(tmp, LIB)
-    # the matrix-core ceiling probe (a standalone executable, not part of the library)
-    tmp = PROBE + ".tmp"
-    _run([cc] + COMMON + ["-o", tmp, os.path.join(CSRC, "mfma_ceiling_probe.hip")])
-    os.replace(tmp, PROBE)
+    # the ceiling probes (standalone executables, not part of the library)
+    for name in PROBES:
+        exe = os.path.join(HERE, name)
+        _run([cc] + COMMON + ["-o", exe + ".tmp", os.path.join(CSRC, name + ".hip")])
+        os.replace(exe + ".tmp", exe)
     return LIB
 
 
