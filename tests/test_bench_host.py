@@ -100,3 +100,17 @@ def test_clock_sampler_reports_a_missing_tool(monkeypatch):
     s = bench.ClockSampler(interval=0.0).start()
     rep = s.stop()
     assert "error" in rep and "FileNotFoundError" in rep["error"]
+
+
+def test_ceiling_probes_are_built_beside_the_library():
+    from long_sequence_dense_amd import build
+    assert set(build.PROBES) == {"mfma_ceiling_probe", "hbm_ceiling_probe"}
+    for name in build.PROBES:
+        assert os.path.exists(os.path.join(ROOT, "long_sequence_dense_amd", "csrc", name + ".hip"))
+
+
+def test_missing_probes_are_skipped_not_fatal(monkeypatch, tmp_path):
+    # the bench reports None for a probe executable that is not built
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.bw_ceiling() is None
+    assert bench.mfma_ceiling() is None
