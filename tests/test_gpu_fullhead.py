@@ -3,7 +3,8 @@ the benchmark's launch configuration): every query row of two full heads of
 the BF16 workload and of the FP4 workload against the fp64 oracle, with the
 method's bars (max-abs 2e-2, mean-abs 2e-3; the FP4-QK path against the
 oracle attention on the oracle's own codes, which are checked bit-exact
-against the GPU's first).
+against the GPU's first).  The same for the shorter BF16 workloads: the whole
+output of 24 x 8192 and two whole heads of 40 x 36,480.
 
 Also the FP4-QK error in the terms "Pika H3 Flex in FastVideo" section
 "FP4 attention" uses for its kernel (close to the quantization error itself):
@@ -160,3 +161,41 @@ def test_fp4qk_whole_head(torch, fp4_run, i):
         say("  fp4qk head %d: ||O_gpu - O_same_codes|| / ||O_same_codes - O_exact|| = %.3e / %.3e = %.4f %%"
             % (h, kernel, quant, 100.0 * kernel / quant))
         assert kernel <= 0.01 * quant
+
+
+# The two shorter BF16 workloads in the same terms: every row of every head of
+# the 24 x 8192 workload (its whole output) and every row of the first and
+# last head of the 5-second clip (40 x 36,480).
+SHORT_CASES = {"mid": list(range(24)), "clip5s": [0, 39]}
+
+
+@pytest.fixture(scope="module")
+def short_runs(torch):
+    from long_sequence_dense_amd import binding
+    runs = {}
+    for name, heads in SHORT_CASES.items():
+        c = inputs.CONFIGS[name]
+        say("case whole heads: %s H=%d L=%d bf16 (generate)" % (name, c.H, c.L))
+        d = inputs.make_inputs(name)
+        q, k, v = (bf16_dev(torch, d[n]) for n in ("q", "k", "v"))
+        o = torch.full((c.H, c.L, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((c.H, c.L), float("nan"), dtype=torch.float32, device="cuda")
+        binding.attn_fwd_bf16(q, k, v, o, lse, softmax_scale=d["scale"])
+        torch.cuda.synchronize()
+        assert not torch.isnan(o).any().item()
+        runs[name] = {"o": host_heads(torch, o, heads),
+                      "lse": host_heads(torch, lse, heads).numpy().astype(np.float64),
+                      "q": d["q"][heads], "k": d["k"][heads], "v": d["v"][heads], "scale": d["scale"]}
+        del q, k, v, o, lse, d
+        torch.cuda.empty_cache()
+    return runs
+
+
+@pytest.mark.parametrize("name", sorted(SHORT_CASES))
+def test_bf16_shorter_workloads_whole_heads(torch, short_runs, name):
+    r = short_runs[name]
+    heads = SHORT_CASES[name]
+    say("case %s whole heads %s: oracle on all rows (%d workers)" % (name, heads, workers()))
+    for i, h in enumerate(heads):
+        oref, lref = oracle_head(f64(r["q"][i]), f64(r["k"][i]), f64(r["v"][i]), r["scale"])
+        compare("%s head %d O" % (name, h), o_f64(torch, r["o"][i]), oref, r["lse"][i], lref)
